@@ -1,0 +1,19 @@
+"""CPU oracle for the FP8 block-scaled GEMM (NT) and its M-grouped MoE forms.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The library's GPU path
+never calls it and shares no code with it.
+
+The oracle is plain numpy in fp64.  See ``fp8_gemm`` for the definitions and
+the passages of the DeepGEMM pages each step follows.
+"""
+from .fp8_gemm import (  # noqa: F401
+    E4M3_VALUES,
+    decode_e4m3,
+    bf16_bits_to_f64,
+    round_f64_to_bf16_bits,
+    gemm_nt_acc,
+    gemm_nt,
+    m_grouped_contiguous,
+    m_grouped_masked,
+)
