@@ -1,0 +1,118 @@
+/*
+ * dg.h -- FP8 (OCP e4m3) GEMM with fine-grained block scaling for AMD MI355X (gfx950).
+ *
+ * What the calls compute (DeepGEMM pages: likun.im/craft/deepgemm.html, section
+ * 一 "the GEMM family", D = C + A @ B in the NT layout, and section 二, the
+ * register_apis listing of the dense call and the two M-grouped MoE calls;
+ * aitangshan.cn/news/1491278, "4. FP8 精度优化的核心": each block's GEMM result is
+ * multiplied by that block's scale factors):
+ *
+ *   D[m,n] = bf16_rne( C[m,n] + sum_kb sa[kb][m] * sb[n/128][kb]
+ *                                      * sum_{k in block kb} A[m,k] * B[n,k] )
+ *
+ * with kb running over the K/128 blocks of 128 consecutive K indices.  A and B
+ * hold e4m3 codes; every product is summed in fp32 on the GPU ("fp32
+ * accumulation"); each block's partial sum is multiplied by its A scale (one
+ * per row per block, "1x128") and its B scale (one per 128x128 block) and added
+ * to an fp32 total; C is added and the total is rounded once to bf16 (round to
+ * nearest, ties to even).
+ *
+ * Layouts (every array row-major, every pointer a device pointer on the
+ * current HIP device, owned by the caller; the library keeps no pointer after
+ * the call returns):
+ *   a    uint8  [M][K]            e4m3 codes, K contiguous            (16-byte aligned)
+ *   sfa  float  [K/128][M]        A scales, M contiguous ("MN-major") (4-byte aligned)
+ *   b    uint8  [N][K]            e4m3 codes, K contiguous ("NT")     (16-byte aligned)
+ *   sfb  float  [ceil(N/128)][K/128]  B scales                        (4-byte aligned)
+ *   c    bf16   [M][N]            bit patterns; NULL means C = 0; may equal d
+ *   d    bf16   [M][N]            output                              (2-byte aligned)
+ * K must be a multiple of 128.  The grouped forms add a leading group axis to
+ * B and sfb: b [G][N][K], sfb [G][ceil(N/128)][K/128].
+ *
+ * Calls are asynchronous: they validate their arguments on the host, enqueue
+ * one or more kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ * return without waiting.  Device-resident control data (grouped_layout,
+ * masked_m) is read only by the kernels, so no call synchronises with the
+ * device and every call may be captured in a HIP graph once dg_init() has run
+ * on the device.  Faults inside a kernel surface at the caller's next
+ * synchronisation, as for any HIP kernel.
+ *
+ * Errors: an invalid argument returns DG_ERR_INVALID_ARG and launches nothing;
+ * a shape the kernels do not handle returns DG_ERR_UNSUPPORTED; a failing HIP
+ * call returns DG_ERR_HIP.  dg_last_error() then describes the failure (per
+ * host thread).  No C++ exception crosses this interface.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1,
+  DG_ERR_UNSUPPORTED = -2,
+  DG_ERR_HIP = -3
+} dg_status;
+
+/* Dense FP8 GEMM, NT layout: D[M][N] = C + A[M][K] . B[N][K]^T with 1x128 A
+ * scales and 128x128 B scales (likun.im section 一 naming: "fp8_gemm_nt";
+ * aitangshan.cn usage example: a, a's scales, b, b's scales, c, out).
+ * M == 0 or N == 0 is a successful no-op; K == 0 gives D = C.
+ * Returns a dg_status. */
+int dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const void* c, void* d, int M, int N, int K, void* stream);
+
+/* M-grouped GEMM, contiguous layout (likun.im section 二:
+ * "m_grouped_..._gemm_nt_contiguous" taking grouped_layout): the rows of every
+ * expert are concatenated along M.  grouped_layout is a device int32 array of
+ * M entries; row m is computed with expert grouped_layout[m]'s B and sfb.
+ * Rows come in aligned blocks of 128 (rows 128*i .. 128*i+127); within one
+ * block every row whose id lies in [0, num_groups) must carry the same id.
+ * Rows whose id lies outside [0, num_groups) (for example -1 on padding) are
+ * not written.  a [M][K], sfa [K/128][M], b [num_groups][N][K],
+ * sfb [num_groups][ceil(N/128)][K/128], c and d [M][N].
+ * Returns a dg_status. */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
+                                        const float* sfb, const void* c, void* d, int M, int N,
+                                        int K, int num_groups, const int32_t* grouped_layout,
+                                        void* stream);
+
+/* M-grouped GEMM, masked layout (likun.im section 二:
+ * "m_grouped_..._gemm_nt_masked" taking masked_m and expected_m; zwt0204
+ * DeepGEMM deep dive: the masked layout serves inference decoding).  Every
+ * group g owns max_m rows; only its first min(max(masked_m[g], 0), max_m)
+ * rows are computed and written, the others are left untouched.  masked_m is a
+ * device int32 array of num_groups entries, read only by the kernel.
+ * expected_m is a host-side hint of the typical masked_m; it only steers the
+ * launch configuration and never changes which rows are computed.
+ * a [G][max_m][K], sfa [G][K/128][max_m], b [G][N][K], sfb [G][ceil(N/128)][K/128],
+ * c and d [G][max_m][N].  Returns a dg_status. */
+int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b,
+                                    const float* sfb, const void* c, void* d, int max_m, int N,
+                                    int K, int num_groups, const int32_t* masked_m,
+                                    int expected_m, void* stream);
+
+/* Prepares per-device state for the current HIP device (device properties and
+ * the split-K workspace, allocated once and kept until the process ends).
+ * Calls above do this lazily on first use; call dg_init() first when the
+ * first call would otherwise happen inside HIP graph capture.
+ * Returns a dg_status. */
+int dg_init(void);
+
+/* Message describing the last non-DG_OK status returned on this host thread
+ * (empty string if none).  The pointer stays valid until the next call on
+ * this thread. */
+const char* dg_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

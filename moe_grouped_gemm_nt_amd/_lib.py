@@ -1,0 +1,137 @@
+"""ctypes binding of libdg.so (the C ABI in include/dg.h).
+
+Argument marshalling only: torch tensors in, device pointers and the current
+HIP stream out.  Every step of the computation runs in the library's kernels;
+there is no fallback path.  A missing library raises at first use."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libdg.so")
+
+DG_OK = 0
+DG_ERR_INVALID_ARG = -1
+DG_ERR_UNSUPPORTED = -2
+DG_ERR_HIP = -3
+
+EXPORTED = [
+    "dg_fp8_gemm_nt",
+    "dg_m_grouped_fp8_gemm_nt_contiguous",
+    "dg_m_grouped_fp8_gemm_nt_masked",
+    "dg_init",
+    "dg_last_error",
+    "dg_version",
+]
+
+_lock = threading.Lock()
+_lib = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libdg.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m moe_grouped_gemm_nt_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, fp, i32p, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+        lib.dg_fp8_gemm_nt.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp]
+        lib.dg_fp8_gemm_nt.restype = ci
+        lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, vp]
+        lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ci
+        lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
+        lib.dg_m_grouped_fp8_gemm_nt_masked.restype = ci
+        lib.dg_init.argtypes = []
+        lib.dg_init.restype = ci
+        lib.dg_last_error.argtypes = []
+        lib.dg_last_error.restype = ctypes.c_char_p
+        lib.dg_version.argtypes = []
+        lib.dg_version.restype = ci
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, status: int):
+    if status != DG_OK:
+        raise DGError(fn, status, (load().dg_last_error() or b"").decode())
+
+
+_CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+_BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t, name, dtypes, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} must not be None")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def dg_init() -> None:
+    _check("dg_init", load().dg_init())
+
+
+def dg_version() -> int:
+    return load().dg_version()
+
+
+def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """d[M][N] = bf16(c + a[M][K] . b[N][K]^T) with sfa [K/128][M], sfb [ceil(N/128)][K/128]."""
+    M, K = a.shape
+    N = b.shape[0]
+    _check("dg_fp8_gemm_nt", load().dg_fp8_gemm_nt(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:
+    """Contiguous M-grouped form: a [M][K], b [G][N][K], grouped_layout int32 [M]."""
+    M, K = a.shape
+    G, N, _ = b.shape
+    _check("dg_m_grouped_fp8_gemm_nt_contiguous", load().dg_m_grouped_fp8_gemm_nt_contiguous(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, G,
+        _ptr(grouped_layout, "grouped_layout", (torch.int32,)), _stream(stream)))
+
+
+def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, c, d, masked_m, expected_m, stream=None) -> None:
+    """Masked M-grouped form: a [G][max_m][K], b [G][N][K], masked_m int32 [G] on the device."""
+    G, max_m, K = a.shape
+    N = b.shape[1]
+    _check("dg_m_grouped_fp8_gemm_nt_masked", load().dg_m_grouped_fp8_gemm_nt_masked(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), max_m, N, K, G,
+        _ptr(masked_m, "masked_m", (torch.int32,)), int(expected_m), _stream(stream)))

@@ -1,0 +1,239 @@
+// Host side of the C ABI declared in include/dg.h: argument validation,
+// launch-configuration choice, per-device state and error reporting.
+//
+// Configuration choice (the pages' host heuristics pick a kernel layout and
+// launch shape per problem; prefill and decode shapes get different kernels,
+// zwt0204 DeepGEMM deep dive, "它的核心思路" point 2): large problems take the
+// MFMA-oriented 128x128 tile; decode shapes whose tile count cannot fill the
+// 256 compute units take the 64x64 tile with K split across workgroups, so
+// that enough workgroups stream B from HBM at once.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kWorkspaceBytes = size_t(64) << 20;    // split-K partial tiles
+constexpr int kMaxCounters = 1 << 16;                    // split-K tiles per call
+
+struct DeviceState {
+  bool ready = false;
+  int num_cus = 0;
+  float* workspace = nullptr;
+  int32_t* counters = nullptr;
+};
+
+DeviceState g_dev[kMaxDevices];
+std::mutex g_mu;
+
+int get_device_state(DeviceState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  DeviceState& st = g_dev[dev];
+  if (!st.ready) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!st.ready) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+      if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(DG_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950 only", dev, prop.gcnArchName);
+      st.num_cus = prop.multiProcessorCount;
+      e = hipMalloc(&st.workspace, kWorkspaceBytes);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace): %s", hipGetErrorString(e));
+      e = hipMalloc(&st.counters, sizeof(int32_t) * kMaxCounters);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(counters): %s", hipGetErrorString(e));
+      e = hipMemset(st.counters, 0, sizeof(int32_t) * kMaxCounters);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "clearing split-K counters: %s", hipGetErrorString(e));
+      st.ready = true;
+    }
+  }
+  *out = &st;
+  return DG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(const void* a, const float* sfa, const void* b, const float* sfb, const void* c,
+                 void* d, int M, int N, int K) {
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_INVALID_ARG, "a, sfa, b, sfb and d must not be NULL");
+  if (M < 0 || N < 0 || K < 0) return fail(DG_ERR_INVALID_ARG, "negative size (M=%d N=%d K=%d)", M, N, K);
+  if (K % 128 != 0) return fail(DG_ERR_INVALID_ARG, "K=%d is not a multiple of 128", K);
+  if (!aligned(a, 16) || !aligned(b, 16)) return fail(DG_ERR_INVALID_ARG, "a and b must be 16-byte aligned");
+  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return fail(DG_ERR_INVALID_ARG, "sfa and sfb must be 4-byte aligned");
+  if (!aligned(d, 2) || (c && !aligned(c, 2))) return fail(DG_ERR_INVALID_ARG, "c and d must be 2-byte aligned");
+  return DG_OK;
+}
+
+struct Choice {
+  int cfg;
+  int splits;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+// rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
+Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
+  Choice ch{dg::kCfg128x128, 1};
+  const int KB = K / 128;
+  if (mode == dg::kDense && rows <= 64) {
+    ch.cfg = dg::kCfg64x64;
+    const int tiles = ((rows + 63) / 64) * ((N + 63) / 64);
+    int splits = 1;
+    while (tiles * splits * 2 <= 2 * num_cus && splits * 2 <= KB && KB / (splits * 2) >= 4) splits *= 2;
+    ch.splits = splits;
+  }
+  (void)groups;
+  const int forced = env_int("DG_FORCE_CONFIG", -1);
+  if (forced >= 0 && forced < dg::kNumConfigs) ch.cfg = forced;
+  const int fs = env_int("DG_FORCE_SPLITS", 0);
+  if (fs > 0 && mode != dg::kMasked) ch.splits = fs;
+  return ch;
+}
+
+int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
+  DeviceState* st = nullptr;
+  int s = get_device_state(&st);
+  if (s != DG_OK) return s;
+  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus);
+  const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
+  const int KB = p.K / 128;
+  if (ch.splits > KB && KB > 0) ch.splits = KB;
+  if (ch.splits < 1 || KB == 0) ch.splits = 1;
+  p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
+  p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
+  if (ch.splits > 1) {
+    const long long tiles = (long long)p.tiles_m * p.tiles_n;
+    const long long need = tiles * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
+    if (tiles > kMaxCounters || need > (long long)kWorkspaceBytes) ch.splits = 1;
+  }
+  p.splits = ch.splits;
+  p.workspace = st->workspace;
+  p.counters = st->counters;
+  long long items;
+  if (mode == dg::kMasked) {
+    items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
+    const long long cap = (long long)st->num_cus * 2;
+    if (items > cap) items = cap;
+  } else {
+    items = (long long)p.tiles_m * p.tiles_n * p.splits;
+  }
+  if (items > (1LL << 30)) return fail(DG_ERR_UNSUPPORTED, "problem too large (%lld work items)", items);
+  const int grid = (int)(((items + 7) / 8) * 8);
+  if (env_int("DG_LOG", 0))
+    std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d grid=%d\n", mode, p.rows, p.N,
+                 p.K, p.G, ci.name, p.splits, grid);
+  hipError_t e = dg::launch_gemm(mode, ch.cfg, p, grid, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" int dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const void* c, void* d, int M, int N, int K, void* stream) {
+  int s = check_common(a, sfa, b, sfb, c, d, M, N, K);
+  if (s != DG_OK) return s;
+  if (M == 0 || N == 0) return DG_OK;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.G = 1;
+  return launch(dg::kDense, p, M, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
+                                                   const float* sfb, const void* c, void* d, int M,
+                                                   int N, int K, int num_groups,
+                                                   const int32_t* grouped_layout, void* stream) {
+  int s = check_common(a, sfa, b, sfb, c, d, M, N, K);
+  if (s != DG_OK) return s;
+  if (num_groups < 1) return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be at least 1", num_groups);
+  if (!grouped_layout) return fail(DG_ERR_INVALID_ARG, "grouped_layout must not be NULL");
+  if (!aligned(grouped_layout, 4)) return fail(DG_ERR_INVALID_ARG, "grouped_layout must be 4-byte aligned");
+  if (M == 0 || N == 0) return DG_OK;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.layout = grouped_layout;
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.G = num_groups;
+  return launch(dg::kContiguous, p, M, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b,
+                                               const float* sfb, const void* c, void* d, int max_m,
+                                               int N, int K, int num_groups, const int32_t* masked_m,
+                                               int expected_m, void* stream) {
+  int s = check_common(a, sfa, b, sfb, c, d, max_m, N, K);
+  if (s != DG_OK) return s;
+  if (num_groups < 1) return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be at least 1", num_groups);
+  if (num_groups > 1024) return fail(DG_ERR_UNSUPPORTED, "num_groups=%d exceeds 1024", num_groups);
+  if (!masked_m) return fail(DG_ERR_INVALID_ARG, "masked_m must not be NULL");
+  if (!aligned(masked_m, 4)) return fail(DG_ERR_INVALID_ARG, "masked_m must be 4-byte aligned");
+  if (expected_m < 0) return fail(DG_ERR_INVALID_ARG, "expected_m=%d must not be negative", expected_m);
+  if (max_m == 0 || N == 0) return DG_OK;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.masked_m = masked_m;
+  p.rows = max_m;
+  p.N = N;
+  p.K = K;
+  p.G = num_groups;
+  return launch(dg::kMasked, p, expected_m > 0 ? expected_m : max_m, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int dg_init(void) {
+  DeviceState* st = nullptr;
+  return get_device_state(&st);
+}
+
+extern "C" const char* dg_last_error(void) { return g_err.c_str(); }
+
+extern "C" int dg_version(void) { return 100; }

@@ -1,0 +1,54 @@
+// Internal interface between the host entry points (dg_api.hip) and the
+// gfx950 kernels (fp8_gemm.hip).  Not installed, not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum Mode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Everything one launch needs.  Row counts and strides are in elements.
+struct Params {
+  const uint8_t* a;        // e4m3 codes
+  const float* sfa;        // [KB][rows] (masked: [G][KB][max_m])
+  const uint8_t* b;        // e4m3 codes [N][K] (grouped: [G][N][K])
+  const float* sfb;        // [NB][KB] (grouped: [G][NB][KB])
+  const uint16_t* c;       // bf16 bits or nullptr
+  uint16_t* d;             // bf16 bits
+  const int32_t* layout;   // contiguous: expert id per row
+  const int32_t* masked_m; // masked: valid rows per group
+  float* workspace;        // split-K partial tiles (fp32)
+  int32_t* counters;       // split-K arrival counters, one per output tile, kept at zero between calls
+  int rows;                // dense/contiguous: M; masked: max_m
+  int N;
+  int K;
+  int G;                   // groups (1 for dense)
+  int tiles_m;             // ceil(rows / BM)
+  int tiles_n;             // ceil(N / BN)
+  int splits;              // split-K factor (>= 1)
+};
+
+// Tile configurations compiled into the library.
+enum Config : int {
+  kCfg128x128 = 0,   // 128x128 tile, 4 waves of 64x64: large GEMMs
+  kCfg64x64 = 1,     // 64x64 tile, 4 waves of 64x16: decode shapes, split-K capable
+  kCfg256x128 = 2,   // 256x128 tile, 4 waves of 128x64
+  kCfg128x64 = 3,    // 128x64 tile, 4 waves of 64x32
+  kNumConfigs
+};
+
+struct ConfigInfo {
+  int bm, bn, threads;
+  const char* name;
+};
+
+const ConfigInfo& config_info(int cfg);
+
+// Enqueues the kernel for `mode` with configuration `cfg` on `stream`.
+// `grid` is the number of workgroups; the kernels walk tiles (persistently
+// when grid is smaller than the tile count).
+hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
+
+}  // namespace dg

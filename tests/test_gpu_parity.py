@@ -1,0 +1,297 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Exact-regime inputs (small-integer codes, power-of-two scales) must match bit
+for bit; random inputs must meet |d - ref| <= 8e-3 |ref| + 1e-3 rms(ref) and a
+relative Frobenius error <= 2e-3.  Full-size workloads are checked on sampled
+rows that the oracle computes one by one."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import oracle
+from tests.gpu_util import (SENTINEL, bf16_bits_dev, bits_host, check_tolerance, dev,
+                            sentinel_like)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_grouped_gemm_nt_amd as m
+    m.dg_init()
+    return m
+
+
+def run_dense(dg, p, c_dev=None, out=None):
+    a, b = dev(p.a), dev(p.b)
+    sfa, sfb = dev(p.sfa), dev(p.sfb)
+    c = c_dev if c_dev is not None else (bf16_bits_dev(p.c) if p.c is not None else None)
+    d = out if out is not None else sentinel_like((p.M, p.N))
+    dg.dg_fp8_gemm_nt(a, sfa, b, sfb, c, d)
+    torch.cuda.synchronize()
+    return bits_host(d)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# dense
+# ---------------------------------------------------------------------------
+def test_dense_config0_full(dg):
+    log("case: dense config 0 (128x256x512) full oracle")
+    p = inputgen.make_config(0)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    check_tolerance(got, ref, "config0")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_dense_config0_seeds_exact_regime(dg, seed):
+    log(f"case: exact regime 128x256x512 seed {seed}")
+    p = inputgen.exact_dense(128, 256, 512, seed=seed)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    assert np.array_equal(got, ref)
+
+
+def test_dense_config1_decode_full(dg):
+    log("case: dense config 1 (64x2112x7168, C) full oracle")
+    p = inputgen.make_config(1)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    check_tolerance(got, ref, "config1")
+
+
+def test_dense_decode_exact_regime(dg):
+    log("case: exact regime 64x2112x7168")
+    p = inputgen.exact_dense(64, 2112, 7168, seed=4)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 8, 128), (7, 64, 256), (64, 2112, 128), (100, 200, 256), (129, 136, 384),
+    (257, 300, 640), (33, 130, 1024), (500, 520, 256), (16, 4096, 1024),
+])
+def test_dense_edge_shapes_exact(dg, M, N, K):
+    log(f"case: exact edge shape {M}x{N}x{K}")
+    p = inputgen.exact_dense(M, N, K, seed=M + N)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
+
+
+def test_dense_subnormal_codes_exact(dg):
+    log("case: subnormal codes 70x90x512")
+    p = inputgen.exact_subnormal_dense(70, 90, 512, seed=8)
+    got = run_dense(dg, p)
+    assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb))
+
+
+@pytest.mark.parametrize("M,N,K,pow2", [(200, 384, 1536, False), (64, 520, 2048, True), (300, 1000, 512, False)])
+def test_dense_random_tolerance(dg, M, N, K, pow2):
+    log(f"case: random {M}x{N}x{K} pow2={pow2}")
+    p = inputgen.make_dense(M, N, K, seed=3, b_std=0.02, c_std=0.1, pow2=pow2)
+    got = run_dense(dg, p)
+    check_tolerance(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"{M}x{N}x{K}")
+
+
+def test_dense_in_place_c_equals_d(dg):
+    log("case: in-place c == d")
+    p = inputgen.exact_dense(96, 200, 512, seed=12)
+    cd = bf16_bits_dev(p.c)
+    got = run_dense(dg, p, c_dev=cd, out=cd)
+    assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+def test_dense_k_zero_gives_c(dg):
+    log("case: K = 0")
+    rng = np.random.default_rng(0)
+    c = inputgen.bf16_bits_from_f32(rng.standard_normal((5, 9)).astype(np.float32))
+    a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((9, 0), dtype=torch.uint8, device="cuda")
+    sfa = torch.zeros((0, 5), dtype=torch.float32, device="cuda")
+    sfb = torch.zeros((1, 0), dtype=torch.float32, device="cuda")
+    # empty tensors may carry null data pointers: give the library valid ones
+    a = torch.zeros((5, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    d = sentinel_like((5, 9))
+    import moe_grouped_gemm_nt_amd._lib as L
+    lib = L.load()
+    scratch = torch.zeros(64, dtype=torch.float32, device="cuda")
+    rc = lib.dg_fp8_gemm_nt(scratch.data_ptr(), scratch.data_ptr(), scratch.data_ptr(), scratch.data_ptr(),
+                            bf16_bits_dev(c).data_ptr(), d.data_ptr(), 5, 9, 0, None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(d), c)
+    del a, b, sfa, sfb
+
+
+def test_dense_split_k_forced_matches(dg, monkeypatch):
+    log("case: forced split-K")
+    p = inputgen.exact_dense(64, 640, 4096, seed=13)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    for splits in ["1", "2", "3", "8"]:
+        monkeypatch.setenv("DG_FORCE_SPLITS", splits)
+        got = run_dense(dg, p)
+        assert np.array_equal(got, ref), splits
+    monkeypatch.delenv("DG_FORCE_SPLITS")
+
+
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3"])
+def test_dense_every_tile_config(dg, monkeypatch, cfg):
+    log(f"case: forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = inputgen.exact_dense(300, 520, 768, seed=14)
+    got = run_dense(dg, p)
+    assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+    q = inputgen.make_dense(200, 300, 1024, seed=15, b_std=0.02, c_std=0.1, pow2=False)
+    check_tolerance(run_dense(dg, q), oracle.gemm_nt(q.a, q.sfa, q.b, q.sfb, q.c), f"cfg{cfg}")
+
+
+@pytest.mark.slow
+def test_dense_config2_prefill_sampled(dg):
+    log("case: dense config 2 (4096x7168x16384) sampled rows")
+    p = inputgen.make_config(2)
+    got = run_dense(dg, p)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 2047, 2048, 4095],
+                                     rng.integers(0, p.M, size=24)]))
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, None, rows=rows)
+    check_tolerance(got[rows], ref, "config2 sampled")
+
+
+@pytest.mark.slow
+def test_dense_prefill_exact_regime_sampled(dg):
+    log("case: exact regime 1024x7168x16384 sampled")
+    p = inputgen.exact_dense(1024, 7168, 16384, seed=16, e_min=-1, e_span=2)
+    got = run_dense(dg, p)
+    rows = np.array([0, 5, 130, 511, 700, 1023])
+    assert np.array_equal(got[rows], oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c, rows=rows))
+
+
+# ---------------------------------------------------------------------------
+# contiguous
+# ---------------------------------------------------------------------------
+def run_contig(dg, p, c=None):
+    d = sentinel_like((p.M, p.N))
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb),
+                                           c, d, dev(p.grouped_layout))
+    torch.cuda.synchronize()
+    return bits_host(d)
+
+
+def test_contiguous_small_random(dg):
+    log("case: contiguous 4 experts, N=384, K=1024")
+    p = inputgen.make_contiguous(4, 384, 1024, 700, seed=1)
+    got = run_contig(dg, p)
+    ref, written = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.grouped_layout)
+    assert written.all()
+    check_tolerance(got, ref, "contiguous small")
+
+
+def test_contiguous_exact_with_padding_ids_and_empty_expert(dg):
+    log("case: contiguous exact, -1 padding rows, an empty expert, C")
+    G, N, K = 5, 200, 512
+    rng = np.random.default_rng(3)
+    counts = np.array([130, 0, 7, 256, 1])
+    segs = [((c + 127) // 128) * 128 for c in counts]
+    M = sum(segs)
+    layout = np.full(M, -1, dtype=np.int32)
+    off = 0
+    for g, (cnt, sg) in enumerate(zip(counts, segs)):
+        layout[off:off + cnt] = g
+        off += sg
+    base = inputgen.exact_dense(M, N, K, seed=4)
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=10 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=20 + g).sfb for g in range(G)])
+    c = base.c
+    d = sentinel_like((M, N))
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(base.a), dev(base.sfa), dev(b), dev(sfb),
+                                           bf16_bits_dev(c), d, dev(layout))
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_contiguous(base.a, base.sfa, b, sfb, layout, c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
+    del rng
+
+
+@pytest.mark.slow
+def test_contiguous_config3_sampled(dg):
+    log("case: contiguous config 3 (8 experts, 8192 rows, N=4096, K=7168) sampled rows")
+    p = inputgen.make_config(3)
+    got = run_contig(dg, p)
+    rng = np.random.default_rng(1)
+    starts = np.concatenate([[0], np.cumsum(((p.counts + 127) // 128) * 128)])
+    rows = [s for s in starts[:-1]] + [s + 127 for s in starts[:-1]] + list(rng.integers(0, p.M, size=24))
+    rows = np.unique(np.array(rows))
+    rows = rows[rows < p.M]
+    ref, written = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.grouped_layout, rows=rows)
+    check_tolerance(got[rows][written], ref[written], "config3 sampled")
+
+
+# ---------------------------------------------------------------------------
+# masked
+# ---------------------------------------------------------------------------
+def run_masked(dg, p, expected_m=None, c=None):
+    d = sentinel_like((p.G, p.max_m, p.N))
+    dg.dg_m_grouped_fp8_gemm_nt_masked(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), c, d,
+                                       dev(p.masked_m), p.expected_m if expected_m is None else expected_m)
+    torch.cuda.synchronize()
+    return bits_host(d)
+
+
+def test_masked_small_random(dg):
+    log("case: masked 6 groups, max_m 192, N=256, K=768")
+    p = inputgen.make_masked(6, 192, 256, 768, seed=2, masked_m=[0, 1, 127, 128, 192, 300])
+    got = run_masked(dg, p)
+    ref, written = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m)
+    check_tolerance(got[written], ref[written], "masked small")
+    assert np.all(got[~written] == SENTINEL)
+
+
+@pytest.mark.parametrize("expected_m", [1, 64, 128, 256])
+def test_masked_exact_independent_of_expected_m(dg, expected_m):
+    log(f"case: masked exact, expected_m {expected_m}")
+    G, max_m, N, K = 4, 256, 320, 1024
+    base = inputgen.exact_dense(G * max_m, N, K, seed=31)
+    a = base.a.reshape(G, max_m, K)
+    sfa = np.ascontiguousarray(base.sfa.reshape(K // 128, G, max_m).transpose(1, 0, 2))
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=40 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=50 + g).sfb for g in range(G)])
+    masked_m = np.array([0, 255, 256, 17], dtype=np.int32)
+    c = base.c.reshape(G, max_m, N)
+    d = sentinel_like((G, max_m, N))
+    dg.dg_m_grouped_fp8_gemm_nt_masked(dev(a), dev(sfa), dev(b), dev(sfb), bf16_bits_dev(c), d,
+                                       dev(masked_m), expected_m)
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_masked(a, sfa, b, sfb, masked_m, c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
+
+
+@pytest.mark.slow
+def test_masked_config4_sampled(dg):
+    log("case: masked config 4 (32 experts, max_m 256, N=4096, K=7168) sampled groups")
+    p = inputgen.make_config(4)
+    got = run_masked(dg, p)
+    groups = np.array([0, 5, 13, 31])
+    ref, written = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m, groups=groups)
+    sub = got[groups]
+    check_tolerance(sub[written], ref[written], "config4 sampled")
+    assert np.all(sub[~written] == SENTINEL)
+    # every group: rows past masked_m untouched
+    for g in range(p.G):
+        m = int(min(max(p.masked_m[g], 0), p.max_m))
+        assert np.all(got[g, m:] == SENTINEL)
+        if m:
+            assert not np.any(got[g, :m] == SENTINEL)
