@@ -1,0 +1,263 @@
+"""Throughput of the FP8 block-scaled GEMM (NT) on one MI355X.
+
+One step is one library call over one batch of synthetic inputs already
+resident in HBM.  The headline workload is the dense decode shape
+M=64 N=2112 K=7168 (A ~ N(0,1), B ~ N(0,0.02), 1x128 / 128x128 power-of-two
+scales, bf16 C ~ N(0,0.1)); the other four workloads are reported per shape
+in the same JSON line.  Inputs rotate over enough copies that successive steps
+read from HBM rather than the 256 MB last-level cache; the timed launches are
+replayed from a HIP graph so that host launch cost does not pace the GPU.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA peak (published)
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak (published)
+MALL_BYTES = 256 << 20       # last-level (Infinity) cache to defeat between steps
+HEADLINE = 2                 # 1-based shape index of the headline workload
+
+SHAPES = {
+    1: ("dense_128x256x512", "mfma"),
+    2: ("dense_decode_64x2112x7168", "hbm"),
+    3: ("dense_prefill_4096x7168x16384", "mfma"),
+    4: ("contiguous_8x4096x7168_rows8192", "mfma"),
+    5: ("masked_32x256x4096x7168", "hbm"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(p) -> int:
+    """Bytes that must move once: A and its scales for computed rows, all of
+    B and sfb that computed rows touch, C (if any) and D for computed rows."""
+    import inputgen
+    KB = p.K // 128
+    if isinstance(p, inputgen.Dense):
+        rows = p.M
+        b = p.b.nbytes + p.sfb.nbytes
+        cbytes = (rows * p.N * 2) if p.c is not None else 0
+        return rows * p.K + rows * KB * 4 + b + cbytes + rows * p.N * 2
+    if isinstance(p, inputgen.Contiguous):
+        rows = p.real_rows
+        used = np.unique(p.grouped_layout[p.grouped_layout >= 0])
+        b = sum(p.b[g].nbytes + p.sfb[g].nbytes for g in used)
+        return rows * p.K + rows * KB * 4 + rows * 4 + b + rows * p.N * 2
+    if isinstance(p, inputgen.Masked):
+        m = np.minimum(np.maximum(p.masked_m, 0), p.max_m)
+        rows = int(m.sum())
+        b = sum(p.b[g].nbytes + p.sfb[g].nbytes for g in range(p.G) if m[g] > 0)
+        return rows * p.K + rows * KB * 4 + b + rows * p.N * 2 + p.G * 4
+    raise TypeError(p)
+
+
+class Workload:
+    """Device copies of one generated problem plus the launch closure."""
+
+    def __init__(self, idx, torch, dg, copies=None):
+        import inputgen
+        t0 = time.time()
+        self.p = p = inputgen.make_config(idx - 1, seed=0)
+        self.name, self.bound = SHAPES[idx]
+        self.flops = p.flops
+        self.bytes = algorithmic_bytes(p)
+        per_copy = p.a.nbytes + p.b.nbytes
+        if copies is None:
+            copies = max(1, min(64, math.ceil(2 * MALL_BYTES / per_copy)))
+        self.copies = copies
+        dev = torch.device("cuda")
+
+        def up(x, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(x))
+            return (t.view(dtype) if dtype is not None else t).to(dev)
+
+        a, sfa, b, sfb = up(p.a), up(p.sfa), up(p.b), up(p.sfb)
+        self.sets = []
+        for i in range(copies):
+            s = dict(a=a if i == 0 else a.clone(), sfa=sfa if i == 0 else sfa.clone(),
+                     b=b if i == 0 else b.clone(), sfb=sfb if i == 0 else sfb.clone())
+            if isinstance(p, inputgen.Dense):
+                s["c"] = up(p.c.view(np.int16)).view(torch.bfloat16) if p.c is not None else None
+                s["d"] = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+            elif isinstance(p, inputgen.Contiguous):
+                s["layout"] = up(p.grouped_layout)
+                s["d"] = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+            else:
+                s["masked_m"] = up(p.masked_m)
+                s["d"] = torch.empty((p.G, p.max_m, p.N), dtype=torch.bfloat16, device=dev)
+            self.sets.append(s)
+        self.dg = dg
+        self.kind = type(p).__name__
+        torch.cuda.synchronize()
+        log(f"[bench] {self.name}: generated and uploaded {copies} copies in {time.time() - t0:.1f}s")
+
+    def launch(self, i):
+        s = self.sets[i % self.copies]
+        dg = self.dg
+        if self.kind == "Dense":
+            dg.dg_fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
+        elif self.kind == "Contiguous":
+            dg.dg_m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"], s["layout"])
+        else:
+            dg.dg_m_grouped_fp8_gemm_nt_masked(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"],
+                                               s["masked_m"], self.p.expected_m)
+
+
+def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool = True):
+    """Runs `warmup` untimed steps, then times exactly `steps` steps between a
+    synchronisation on each side.  Returns (total ms, per-step ms)."""
+    for i in range(warmup):
+        w.launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                w.launch(i)
+        torch.cuda.synchronize()
+        graph.replay()                     # one untimed replay: first-replay set-up cost
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                w.launch(i)
+        end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    return total, total / steps
+
+
+def cpu_baseline(p, budget_s=10.0):
+    """The oracle as it stands, on the host cores, on the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    per_call = el / runs
+    return {"value": p.flops / per_call / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole headline workload (M={p.M} N={p.N} K={p.K}), {runs} oracle calls "
+                      f"in {el:.1f}s ({per_call * 1e3:.1f} ms per call)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--shapes", default="1,2,3,4,5", help="comma-separated 1-based workload indices")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_nt_amd as dg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dg.load()
+    dg.dg_init()
+    shapes = [int(s) for s in args.shapes.split(",") if s.strip()]
+    if HEADLINE not in shapes:
+        shapes = [HEADLINE] + shapes
+
+    per_shape = {}
+    head = None
+    for idx in shapes:
+        w = Workload(idx, torch, dg)
+        steps = args.steps
+        if w.flops > 1e11:
+            steps = max(10, min(steps, 50))         # large shapes: keep the timed region short
+        total_ms, ms = time_workload(torch, w, steps, args.warmup, use_graph=not args.no_graph)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = w.bytes / (ms * 1e-3) / 1e9
+        rec = {"ms_per_call": round(ms, 5), "tflops": round(tflops, 2),
+               "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+               "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+               "bound": w.bound, "alg_bytes": int(w.bytes), "flops": float(w.flops),
+               "steps": steps, "copies": w.copies}
+        per_shape[w.name] = rec
+        log(f"[bench] {w.name}: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / FP8_PEAK_TFLOPS:.1f}% "
+            f"of FP8 peak), {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+        if idx == HEADLINE:
+            head = (w, steps, total_ms, ms, tflops, gbs)
+        else:
+            del w
+            torch.cuda.empty_cache()
+
+    w, steps, total_ms, ms, tflops, gbs = head
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(w.name)
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": int(w.bytes), "avg_launch_us": round(ms * 1e3, 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the headline workload")
+        cpu = cpu_baseline(w.p)
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOPS + % of MI355X dense FP8 peak, per shape",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic, seeded (numpy PCG64 seed 0), shapes and distributions of the DeepSeek-V3/R1 GEMMs",
+        "config": {"workload": w.name, "M": w.p.M, "N": w.p.N, "K": w.p.K, "C": True,
+                   "scales": "A 1x128, B 128x128, power-of-two fp32", "rotating_copies": w.copies,
+                   "graph_replay": not args.no_graph, "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_shape": per_shape,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,11 +16,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdg.so")
 SOURCES = ["fp8_gemm.hip", "dg_api.hip"]
 
-# packed fp32 VALU forms are disabled on purpose (see the design notes)
+# packed fp32 VALU forms are disabled on purpose (see the design notes);
+# MFMA results go straight to VGPRs, where the fp32 promotion reads them
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

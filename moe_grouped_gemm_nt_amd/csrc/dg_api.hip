@@ -105,11 +105,13 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   Choice ch{dg::kCfg128x128, 1};
   const int KB = K / 128;
   if (mode == dg::kDense && rows <= 64) {
+    // decode: 64x64 tiles; split K so that every split's K blocks fit the
+    // 8-slot ring (all of them in flight at once) and the workgroups fill the chip
     ch.cfg = dg::kCfg64x64;
     const int tiles = ((rows + 63) / 64) * ((N + 63) / 64);
-    int splits = 1;
-    while (tiles * splits * 2 <= 2 * num_cus && splits * 2 <= KB && KB / (splits * 2) >= 4) splits *= 2;
-    ch.splits = splits;
+    int splits = (KB + 7) / 8;
+    while (splits < KB && tiles * (splits + 1) <= num_cus && (KB + splits) / (splits + 1) >= 4) ++splits;
+    ch.splits = splits < 1 ? 1 : splits;
   }
   (void)groups;
   const int forced = env_int("DG_FORCE_CONFIG", -1);

@@ -32,10 +32,10 @@ struct Params {
 
 // Tile configurations compiled into the library.
 enum Config : int {
-  kCfg128x128 = 0,   // 128x128 tile, 4 waves of 64x64: large GEMMs
-  kCfg64x64 = 1,     // 64x64 tile, 4 waves of 64x16: decode shapes, split-K capable
-  kCfg256x128 = 2,   // 256x128 tile, 4 waves of 128x64
-  kCfg128x64 = 3,    // 128x64 tile, 4 waves of 64x32
+  kCfg128x128 = 0,   // 128x128 tile, 4 waves of 64x64, 4-slot ring: large GEMMs
+  kCfg64x64 = 1,     // 64x64 tile, 4 waves of 64x16, 8-slot ring: decode shapes with split-K
+  kCfg128x64 = 2,    // 128x64 tile, 4 waves of 64x32, 4-slot ring
+  kCfg64x128 = 3,    // 64x128 tile, 4 waves of 64x32, 6-slot ring
   kNumConfigs
 };
 

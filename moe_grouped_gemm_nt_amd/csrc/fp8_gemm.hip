@@ -10,13 +10,16 @@
 // After the last block, C is added and the total is rounded to bf16 (RNE).
 //
 // Work decomposition:
-//   * a workgroup owns a BM x BN output tile; its waves each own a
+//   * a workgroup of four waves owns a BM x BN output tile; each wave owns a
 //     (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in VGPRs;
-//   * A and B K-blocks stream HBM -> LDS with 16-byte coalesced loads into a
-//     two-stage ring, the next stage in flight while the current one feeds
-//     the MFMAs; LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by
-//     row so that fragment reads are free of bank conflicts;
-//   * the A scales of the tile's rows for each K block travel with the stage;
+//   * A and B K-blocks travel HBM -> LDS through the direct global->LDS path
+//     (global_load_lds_dwordx4: no VGPR staging) into a ring of NSLOT slots,
+//     so up to NSLOT-1 K-blocks are in flight while one feeds the MFMAs; each
+//     wave waits only for its own loads of the block it is about to use
+//     (s_waitcnt vmcnt(n)) and a bare s_barrier publishes them; LDS rows are
+//     128 bytes with 16-byte chunks XOR-swizzled by row so fragment reads are
+//     free of bank conflicts; the A scales of the tile's rows and each wave's
+//     B scale ride in the same slot;
 //   * workgroups walk a list of work items (tile, K split); the list is split
 //     into 8 contiguous ranges, one per XCD (the hardware deals workgroups to
 //     the XCDs round-robin), so that tiles sharing A rows or B columns run on
@@ -40,6 +43,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int KBLK = 128;        // K block of the scales and of one MFMA
 constexpr int MAX_GROUPS_LDS = 1024;
@@ -55,7 +59,54 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+// s_waitcnt with vmcnt <= N and all LDS reads of this wave complete
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Runtime-selected wait: vmcnt <= n * LPS for n in [0, MAXN].
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN >= 0) {
+    if (n >= MAXN) {
+      wait_vm_lgkm0<LPS * MAXN>();
+      return;
+    }
+    wait_stages<LPS, MAXN - 1>(n);
+  }
+}
+
+// Direct global->LDS loads.  Lane l's bytes land at LDS address m0 + size*l.
+// Written as inline asm so that the compiler does not treat every later LDS
+// read as dependent on every load in flight (it cannot tell the ring slots
+// apart and would wait for all of them); the kernel waits on vmcnt itself.
+// One wait state separates the M0 write from the load that uses it.
+__device__ __forceinline__ void dma_16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  // the C-style cast is an address-space cast: generic -> LDS offset
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)(p));
+}
+
+// barrier that does not wait for outstanding global->LDS loads; the caller has
+// already waited for the ones it needs.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
 struct Shape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -66,37 +117,31 @@ struct Shape {
   static constexpr int A_BYTES = BM * KBLK;
   static constexpr int B_BYTES = BN * KBLK;
   static constexpr int SA_OFF = A_BYTES + B_BYTES;
-  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
-  static constexpr int A_CHUNKS = BM * 8;       // 16-byte chunks per stage
-  static constexpr int B_CHUNKS = BN * 8;
-  static constexpr int LA = (A_CHUNKS + NT - 1) / NT;
-  static constexpr int LB = (B_CHUNKS + NT - 1) / NT;
+  static constexpr int SA_PER_WAVE = BM / 4 + 4;      // BM/4 row scales, this wave's B scale, pad
+  static constexpr int SLOT = A_BYTES + B_BYTES + NWAVES * SA_PER_WAVE * 4;
+  static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
+  static constexpr int B_INSTR = BN / 8 / NWAVES;
+  static constexpr int LPS = A_INSTR + B_INSTR + 1;   // loads per wave per K block
+  static_assert(NWAVES == 4, "four waves per workgroup");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must sit in one 128-wide B scale block");
-  static_assert(BM % 4 == 0 && BM / 4 <= NT, "A scales are staged as float4 by the first BM/4 threads");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "every wave issues the same number of loads");
+  static_assert(BM <= 128, "row scales plus the B scale fit one 64-lane load per wave");
+  static_assert((NSLOT - 1) * LPS < 64, "outstanding loads must fit the 6-bit vmcnt");
 };
 
-// Per-work-item geometry resolved by the tile walker.
-struct Item {
-  int valid;
-  int group;      // expert (grouped forms), 0 for dense
-  int mt, nt;     // tile coordinates
-  int split;      // K split index
-  int tile_id;    // linear output tile id (split-K counters)
-  int rows_lim;   // rows [0, rows_lim) of the operand may be computed (masked: masked_m)
-};
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE>
-__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE>
+__global__ void __launch_bounds__(256)
 fp8_gemm_nt_kernel(Params p) {
-  using S = Shape<BM, BN, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
+  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSLOT * S::SLOT];
   __shared__ int s_prefix[MODE == kMasked ? MAX_GROUPS_LDS + 1 : 1];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_base = lds_u32(smem);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int KB = p.K / KBLK;
@@ -124,65 +169,61 @@ fp8_gemm_nt_kernel(Params p) {
 
   const int slots = (gridDim.x + 7) / 8;          // workgroups per XCD
   const int xcd = blockIdx.x % 8;
-  const int slot = blockIdx.x / 8;
+  const int slot_id = blockIdx.x / 8;
   const int per_xcd = (total + 7) / 8;
   const int w_begin = xcd * per_xcd;
   const int w_end = min(total, w_begin + per_xcd);
   int g_cur = 0;                                   // masked walker state
 
-  for (int w = w_begin + slot; w < w_end; w += slots) {
+  for (int w = w_begin + slot_id; w < w_end; w += slots) {
     // ---- resolve the work item ---------------------------------------------
-    Item it;
-    it.valid = 1;
-    it.group = 0;
-    it.split = 0;
-    it.rows_lim = p.rows;
+    int group = 0, mt, nt, split = 0, tile_id = 0, rows_lim = p.rows;
     if constexpr (MODE == kMasked) {
       while (w >= s_prefix[g_cur + 1]) ++g_cur;
       const int local = w - s_prefix[g_cur];
       int m = p.masked_m[g_cur];
       m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
       const int tm = (m + BM - 1) / BM;
-      it.group = g_cur;
-      it.mt = local % tm;
-      it.nt = local / tm;
-      it.rows_lim = m;
-      it.tile_id = 0;
+      group = g_cur;
+      mt = local % tm;
+      nt = local / tm;
+      rows_lim = m;
     } else {
       const int tile = w / p.splits;
-      it.split = w % p.splits;
-      it.tile_id = tile;
+      split = w % p.splits;
+      tile_id = tile;
       // grouped ordering: bands of 8 m-tiles sweep across n
       constexpr int GM = 8;
       const int band = tile / (GM * p.tiles_n);
       const int first_m = band * GM;
       const int gm = min(p.tiles_m - first_m, GM);
       const int in_band = tile - band * GM * p.tiles_n;
-      it.mt = first_m + in_band % gm;
-      it.nt = in_band / gm;
+      mt = first_m + in_band % gm;
+      nt = in_band / gm;
       if constexpr (MODE == kContiguous) {
-        // the expert of this 128-row block: the largest id among its rows
+        // the expert of this block of rows: the largest id among its rows
         // (padding rows may carry -1); all valid ids in a block agree
         if (wave == 0) {
           int best = -1;
           for (int r = lane; r < BM; r += 64) {
-            const int row = it.mt * BM + r;
+            const int row = mt * BM + r;
             if (row < p.rows) best = max(best, p.layout[row]);
           }
           for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
           if (lane == 0) s_flag = best;
         }
         __syncthreads();
-        it.group = s_flag;
+        group = s_flag;
         __syncthreads();
-        if (it.group < 0 || it.group >= p.G) continue;   // uniform across the workgroup
+        if (group < 0 || group >= p.G) continue;   // uniform across the workgroup
       }
     }
 
-    const int m0 = it.mt * BM;
-    const int n0 = it.nt * BN;
-    const int kb_begin = (int)(((long long)KB * it.split) / p.splits);
-    const int kb_end = (int)(((long long)KB * (it.split + 1)) / p.splits);
+    const int m0 = mt * BM;
+    const int n0 = nt * BN;
+    const int kb_begin = (int)(((long long)KB * split) / p.splits);
+    const int kb_end = (int)(((long long)KB * (split + 1)) / p.splits);
+    const int kbs = kb_end - kb_begin;
 
     // ---- operand bases -----------------------------------------------------
     const uint8_t* A = p.a;
@@ -193,72 +234,65 @@ fp8_gemm_nt_kernel(Params p) {
     const uint16_t* C = p.c;
     const int a_rows = p.rows;     // rows allocated in this A operand
     if constexpr (MODE == kMasked) {
-      A += (size_t)it.group * p.rows * p.K;
-      SA += (size_t)it.group * KB * p.rows;
-      D += (size_t)it.group * p.rows * p.N;
-      if (C) C += (size_t)it.group * p.rows * p.N;
+      A += (size_t)group * p.rows * p.K;
+      SA += (size_t)group * KB * p.rows;
+      D += (size_t)group * p.rows * p.N;
+      if (C) C += (size_t)group * p.rows * p.N;
     }
     if constexpr (MODE != kDense) {
-      B += (size_t)it.group * p.N * p.K;
-      SB += (size_t)it.group * NB * KB;
+      B += (size_t)group * p.N * p.K;
+      SB += (size_t)group * NB * KB;
     }
 
-    // ---- global -> LDS staging ---------------------------------------------
-    v4i ra[S::LA], rb[S::LB];
-    v4f rsa = {0.f, 0.f, 0.f, 0.f};
-    auto gload = [&](int kb) {
+    const int wrow0 = wm * S::WTM;      // wave's first row in the tile
+    const int wcol0 = wn * S::WTN;
+    int nb = (n0 + wcol0) / 128;
+    nb = nb < NB ? nb : NB - 1;
+
+    // ---- per-lane load addresses (K block 0 of this item) ---------------------
+    // A / B: wave instruction j covers tile rows 8*(wave + 4*j) .. +7; lane l lands
+    // at LDS byte 16*l of that 1 KB piece: row 8*(...) + l/8, physical chunk l%8,
+    // which holds logical chunk (l%8) ^ swz(row).
+    const uint8_t* a_src[S::A_INSTR];
+    const uint8_t* b_src[S::B_INSTR];
 #pragma unroll
-      for (int i = 0; i < S::LA; ++i) {
-        const int q = i * S::NT + tid;
-        if (S::A_CHUNKS % S::NT == 0 || q < S::A_CHUNKS) {
-          const int r = q >> 3, ch = q & 7;
-          int grow = m0 + r;
-          grow = grow < a_rows ? grow : a_rows - 1;     // rows past the end are never stored
-          ra[i] = *reinterpret_cast<const v4i*>(A + (size_t)grow * p.K + (size_t)kb * KBLK + ch * 16);
-        }
-      }
+    for (int j = 0; j < S::A_INSTR; ++j) {
+      const int r = (wave + 4 * j) * 8 + (lane >> 3);
+      int grow = m0 + r;
+      grow = grow < a_rows ? grow : a_rows - 1;       // rows past the end are never stored
+      a_src[j] = A + (size_t)grow * p.K + (size_t)kb_begin * KBLK + (((lane & 7) ^ swz(r)) << 4);
+    }
 #pragma unroll
-      for (int i = 0; i < S::LB; ++i) {
-        const int q = i * S::NT + tid;
-        if (S::B_CHUNKS % S::NT == 0 || q < S::B_CHUNKS) {
-          const int r = q >> 3, ch = q & 7;
-          int gn = n0 + r;
-          gn = gn < p.N ? gn : p.N - 1;
-          rb[i] = *reinterpret_cast<const v4i*>(B + (size_t)gn * p.K + (size_t)kb * KBLK + ch * 16);
-        }
-      }
-      if (tid < BM / 4) {
-        const int r = m0 + tid * 4;
-        const float* src = SA + (size_t)kb * a_rows;
-        if (r + 3 < a_rows && ((a_rows & 3) == 0)) {
-          rsa = *reinterpret_cast<const v4f*>(src + r);
-        } else {
-          rsa.x = src[min(r + 0, a_rows - 1)];
-          rsa.y = src[min(r + 1, a_rows - 1)];
-          rsa.z = src[min(r + 2, a_rows - 1)];
-          rsa.w = src[min(r + 3, a_rows - 1)];
-        }
-      }
-    };
-    auto lstore = [&](int stage) {
-      uint8_t* base = smem + stage * S::STAGE;
+    for (int j = 0; j < S::B_INSTR; ++j) {
+      const int r = (wave + 4 * j) * 8 + (lane >> 3);
+      int gn = n0 + r;
+      gn = gn < p.N ? gn : p.N - 1;
+      b_src[j] = B + (size_t)gn * p.K + (size_t)kb_begin * KBLK + (((lane & 7) ^ swz(r)) << 4);
+    }
+    // scales: lanes < BM/4 load row scales of rows wave*BM/4 + lane, lane BM/4 loads
+    // this wave's B scale
+    const float* s_src;
+    size_t s_stride;                  // elements per K block
+    if (lane < BM / 4) {
+      int grow = m0 + wave * (BM / 4) + lane;
+      grow = grow < a_rows ? grow : a_rows - 1;
+      s_src = SA + (size_t)kb_begin * a_rows + grow;
+      s_stride = a_rows;
+    } else {
+      s_src = SB + (size_t)nb * KB + kb_begin;
+      s_stride = 1;
+    }
+
+    auto issue = [&](int i) {       // i: K block index relative to kb_begin
+      const uint32_t slot = smem_base + (uint32_t)((i % NSLOT) * S::SLOT);
 #pragma unroll
-      for (int i = 0; i < S::LA; ++i) {
-        const int q = i * S::NT + tid;
-        if (S::A_CHUNKS % S::NT == 0 || q < S::A_CHUNKS) {
-          const int r = q >> 3, ch = q & 7;
-          *reinterpret_cast<v4i*>(base + r * KBLK + ((ch ^ swz(r)) << 4)) = ra[i];
-        }
-      }
+      for (int j = 0; j < S::A_INSTR; ++j)
+        dma_16(a_src[j] + (size_t)i * KBLK, slot + (wave + 4 * j) * 1024);
 #pragma unroll
-      for (int i = 0; i < S::LB; ++i) {
-        const int q = i * S::NT + tid;
-        if (S::B_CHUNKS % S::NT == 0 || q < S::B_CHUNKS) {
-          const int r = q >> 3, ch = q & 7;
-          *reinterpret_cast<v4i*>(base + S::A_BYTES + r * KBLK + ((ch ^ swz(r)) << 4)) = rb[i];
-        }
-      }
-      if (tid < BM / 4) *reinterpret_cast<v4f*>(base + S::SA_OFF + tid * 16) = rsa;
+      for (int j = 0; j < S::B_INSTR; ++j)
+        dma_16(b_src[j] + (size_t)i * KBLK, slot + S::A_BYTES + (wave + 4 * j) * 1024);
+      if (lane <= BM / 4)
+        dma_4(s_src + (size_t)i * s_stride, slot + S::SA_OFF + wave * S::SA_PER_WAVE * 4);
     };
 
     // ---- accumulators --------------------------------------------------------
@@ -270,25 +304,24 @@ fp8_gemm_nt_kernel(Params p) {
 
     const int g16 = lane >> 4;          // which 32-byte K slice of the row (operands), row quad (result)
     const int r16 = lane & 15;          // row of A / column of B within a 16-strip
-    const int wrow0 = wm * S::WTM;      // wave's first row in the tile
-    const int wcol0 = wn * S::WTN;
-    int nb = (n0 + wcol0) / 128;
-    nb = nb < NB ? nb : NB - 1;
 
-    if (kb_begin < kb_end) {
-      gload(kb_begin);
-      lstore(0);
-    }
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-      const int stage = (kb - kb_begin) & 1;
-      __syncthreads();
-      const bool more = kb + 1 < kb_end;
-      if (more) gload(kb + 1);
+    // ---- K loop over the slot ring -----------------------------------------------
+    const bool wraps = kbs > NSLOT;
+    const int pre = wraps ? NSLOT - 1 : kbs;
+    for (int i = 0; i < pre; ++i) issue(i);
+    for (int i = 0; i < kbs; ++i) {
+      // loads issued after block i that may stay in flight
+      const int after = min(kbs - 1 - i, wraps ? NSLOT - 2 : NSLOT - 1);
+      wait_stages<S::LPS, NSLOT - 1>(after);
+      bare_barrier();
+      if (wraps && i + NSLOT - 1 < kbs) issue(i + NSLOT - 1);
 
-      const uint8_t* base = smem + stage * S::STAGE;
-      const float sb = SB[(size_t)nb * KB + kb];
+      const uint8_t* base = smem + (i % NSLOT) * S::SLOT;
+      const float* sreg = reinterpret_cast<const float*>(base + S::SA_OFF);
+      const float sb = sreg[wave * S::SA_PER_WAVE + BM / 4];
 
-      v8i bf[S::SN];
+      // fragments of this K block: B for the wave's column strips, A for its row strips
+      v8i bf[S::SN], af[S::SM];
 #pragma unroll
       for (int j = 0; j < S::SN; ++j) {
         const int r = wcol0 + j * 16 + r16;
@@ -298,34 +331,50 @@ fp8_gemm_nt_kernel(Params p) {
         const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * g16 + 1) ^ s) << 4));
         bf[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
+      v4f sc[S::SM];
 #pragma unroll
-      for (int i = 0; i < S::SM; ++i) {
-        const int r = wrow0 + i * 16 + r16;
+      for (int ii = 0; ii < S::SM; ++ii) {
+        const int r = wrow0 + ii * 16 + r16;
         const uint8_t* rp = base + r * KBLK;
         const int s = swz(r);
         const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * g16) ^ s) << 4));
         const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * g16 + 1) ^ s) << 4));
-        const v8i af = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        // scales of this lane's four result rows
-        const v4f sa4 = *reinterpret_cast<const v4f*>(base + S::SA_OFF + (wrow0 + i * 16 + g16 * 4) * 4);
-        const v4f sc = sa4 * sb;
+        af[ii] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        // scales of this lane's four result rows (a 4-row group never straddles a wave block)
+        const int q = wrow0 + ii * 16 + g16 * 4;
+        const v4f sa4 = *reinterpret_cast<const v4f*>(sreg + (q / (BM / 4)) * S::SA_PER_WAVE + q % (BM / 4));
+        sc[ii] = sa4 * sb;
+      }
+      // software pipeline over the wave's sub-tiles: the MFMA of sub-tile t is
+      // issued before the promotion of sub-tile t-(P-1), so P-1 MFMAs are in
+      // flight while the VALU promotes a finished partial
+      constexpr int T = S::SM * S::SN;
+      constexpr int P = 4;
+      v4f part[P];
 #pragma unroll
-        for (int j = 0; j < S::SN; ++j) {
+      for (int t = 0; t < T + P - 1; ++t) {
+        if (t < T) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0, 0, 0);
-          acc[i][j].x = __builtin_fmaf(part.x, sc.x, acc[i][j].x);
-          acc[i][j].y = __builtin_fmaf(part.y, sc.y, acc[i][j].y);
-          acc[i][j].z = __builtin_fmaf(part.z, sc.z, acc[i][j].z);
-          acc[i][j].w = __builtin_fmaf(part.w, sc.w, acc[i][j].w);
+          part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
+                                                                         0, 0, 0, 0, 0, 0);
+        }
+        const int u = t - (P - 1);
+        if (u >= 0) {
+          v4f& a = acc[u / S::SN][u % S::SN];
+          const v4f& q = part[u % P];
+          const v4f& c = sc[u / S::SN];
+          a.x = __builtin_fmaf(q.x, c.x, a.x);
+          a.y = __builtin_fmaf(q.y, c.y, a.y);
+          a.z = __builtin_fmaf(q.z, c.z, a.z);
+          a.w = __builtin_fmaf(q.w, c.w, a.w);
         }
       }
-      if (more) lstore(stage ^ 1);
     }
 
     // ---- split-K: publish the partial, the last split reduces ----------------
     if (p.splits > 1) {
-      float* ws = p.workspace + (size_t)it.tile_id * p.splits * (BM * BN);
-      v4f* mine = reinterpret_cast<v4f*>(ws + (size_t)it.split * (BM * BN));
+      float* ws = p.workspace + (size_t)tile_id * p.splits * (BM * BN);
+      v4f* mine = reinterpret_cast<v4f*>(ws + (size_t)split * (BM * BN));
 #pragma unroll
       for (int i = 0; i < S::SM; ++i)
 #pragma unroll
@@ -334,7 +383,7 @@ fp8_gemm_nt_kernel(Params p) {
       __threadfence();
       __syncthreads();
       if (tid == 0) {
-        const int old = atomicAdd(p.counters + it.tile_id, 1);
+        const int old = atomicAdd(p.counters + tile_id, 1);
         s_flag = (old == p.splits - 1);
       }
       __syncthreads();
@@ -346,54 +395,88 @@ fp8_gemm_nt_kernel(Params p) {
       for (int i = 0; i < S::SM; ++i)
 #pragma unroll
         for (int j = 0; j < S::SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < p.splits; ++s) {
-        const v4f* src = reinterpret_cast<const v4f*>(ws + (size_t)s * (BM * BN));
+      // load BATCH partials at a time (all in flight together), add in split order
+      constexpr int BATCH = (S::SM * S::SN >= 32) ? 1 : 32 / (S::SM * S::SN);
+      for (int s0 = 0; s0 < p.splits; s0 += BATCH) {
+        v4f part[BATCH][S::SM][S::SN];
 #pragma unroll
-        for (int i = 0; i < S::SM; ++i)
+        for (int u = 0; u < BATCH; ++u) {
+          const int s = min(s0 + u, p.splits - 1);
+          const v4f* src = reinterpret_cast<const v4f*>(ws + (size_t)s * (BM * BN));
 #pragma unroll
-          for (int j = 0; j < S::SN; ++j)
-            acc[i][j] += __builtin_nontemporal_load(&src[((wave * S::SM + i) * S::SN + j) * 64 + lane]);
-      }
-      if (tid == 0) p.counters[it.tile_id] = 0;
-    }
-
-    // ---- epilogue: + C, round to bf16, store the rows that belong to the result
+          for (int i = 0; i < S::SM; ++i)
 #pragma unroll
-    for (int i = 0; i < S::SM; ++i) {
+            for (int j = 0; j < S::SN; ++j)
+              part[u][i][j] = __builtin_nontemporal_load(&src[((wave * S::SM + i) * S::SN + j) * 64 + lane]);
+        }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
-        bool ok = row < it.rows_lim;
-        if constexpr (MODE == kContiguous) ok = ok && p.layout[row] == it.group;
-        if (!ok) continue;
+        for (int u = 0; u < BATCH; ++u) {
+          if (s0 + u < p.splits) {
 #pragma unroll
-        for (int j = 0; j < S::SN; ++j) {
-          const int col = n0 + wcol0 + j * 16 + r16;
-          if (col < p.N) {
-            float v = acc[i][j][e];
-            if (C) v += bf16_to_f32(C[(size_t)row * p.N + col]);
-            D[(size_t)row * p.N + col] = f32_to_bf16(v);
+            for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+              for (int j = 0; j < S::SN; ++j) acc[i][j] += part[u][i][j];
           }
         }
       }
+      if (tid == 0) p.counters[tile_id] = 0;
     }
+
+    // ---- epilogue: + C, round to bf16, store the rows that belong to the result
+    // All loads (row ids, C) are issued before any store so their latencies overlap.
+    bool row_ok[S::SM][4];
+#pragma unroll
+    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
+        row_ok[i][e] = row < rows_lim;
+        if constexpr (MODE == kContiguous)
+          row_ok[i][e] = row_ok[i][e] && p.layout[min(row, p.rows - 1)] == group;
+      }
+    if (C) {
+#pragma unroll
+      for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = min(m0 + wrow0 + i * 16 + g16 * 4 + e, p.rows - 1);
+#pragma unroll
+          for (int j = 0; j < S::SN; ++j) {
+            const int col = min(n0 + wcol0 + j * 16 + r16, p.N - 1);
+            acc[i][j][e] += bf16_to_f32(C[(size_t)row * p.N + col]);
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
+#pragma unroll
+        for (int j = 0; j < S::SN; ++j) {
+          const int col = n0 + wcol0 + j * 16 + r16;
+          if (row_ok[i][e] && col < p.N) D[(size_t)row * p.N + col] = f32_to_bf16(acc[i][j][e]);
+        }
+      }
     // the next item reuses the LDS ring
     __syncthreads();
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
 hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
-  constexpr int threads = WAVES_M * WAVES_N * 64;
   switch (mode) {
     case kDense:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, kDense>), dim3(grid), dim3(threads), 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense>), dim3(grid), dim3(256), 0,
+                         stream, p);
       break;
     case kContiguous:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, kContiguous>), dim3(grid), dim3(threads), 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kContiguous>), dim3(grid), dim3(256),
+                         0, stream, p);
       break;
     case kMasked:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, kMasked>), dim3(grid), dim3(threads), 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kMasked>), dim3(grid), dim3(256), 0,
+                         stream, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -402,10 +485,10 @@ hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
 }
 
 const ConfigInfo kConfigs[kNumConfigs] = {
-    {128, 128, 256, "128x128_w2x2"},
-    {64, 64, 256, "64x64_w1x4"},
-    {256, 128, 256, "256x128_w2x2"},
-    {128, 64, 256, "128x64_w2x2"},
+    {128, 128, 256, "128x128_w2x2_s4"},
+    {64, 64, 256, "64x64_w1x4_s8"},
+    {128, 64, 256, "128x64_w2x2_s4"},
+    {64, 128, 256, "64x128_w1x4_s6"},
 };
 
 }  // namespace
@@ -414,10 +497,10 @@ const ConfigInfo& config_info(int cfg) { return kConfigs[cfg]; }
 
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream) {
   switch (cfg) {
-    case kCfg128x128: return launch_cfg<128, 128, 2, 2>(mode, p, grid, stream);
-    case kCfg64x64: return launch_cfg<64, 64, 1, 4>(mode, p, grid, stream);
-    case kCfg256x128: return launch_cfg<256, 128, 2, 2>(mode, p, grid, stream);
-    case kCfg128x64: return launch_cfg<128, 64, 2, 2>(mode, p, grid, stream);
+    case kCfg128x128: return launch_cfg<128, 128, 2, 2, 4>(mode, p, grid, stream);
+    case kCfg64x64: return launch_cfg<64, 64, 1, 4, 8>(mode, p, grid, stream);
+    case kCfg128x64: return launch_cfg<128, 64, 2, 2, 4>(mode, p, grid, stream);
+    case kCfg64x128: return launch_cfg<64, 128, 1, 4, 6>(mode, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
