@@ -4,9 +4,10 @@
 // Configuration choice (the pages' host heuristics pick a kernel layout and
 // launch shape per problem; prefill and decode shapes get different kernels,
 // zwt0204 DeepGEMM deep dive, "它的核心思路" point 2): large problems take the
-// MFMA-oriented 128x128 tile; decode shapes whose tile count cannot fill the
-// 256 compute units take the 64x64 tile with K split across workgroups, so
-// that enough workgroups stream B from HBM at once.
+// MFMA-oriented 128x128 tile; dense decode shapes whose tile count cannot fill
+// the 256 compute units take the 64x64 tile with K split across workgroups, so
+// that enough workgroups stream B from HBM at once, followed by a split-K
+// reduction kernel.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -36,7 +37,7 @@ int fail(int status, const char* fmt, ...) {
 
 constexpr int kMaxDevices = 64;
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;    // split-K partial tiles
-constexpr int kMaxCounters = 1 << 16;                    // split-K tiles per call
+constexpr int kMaxCounters = 1 << 16;                    // split-K output tiles per call
 
 struct DeviceState {
   bool ready = false;
@@ -93,6 +94,7 @@ int check_common(const void* a, const float* sfa, const void* b, const float* sf
 struct Choice {
   int cfg;
   int splits;
+  int kbs;      // K blocks per split (decode configuration)
 };
 
 int env_int(const char* name, int dflt) {
@@ -102,22 +104,31 @@ int env_int(const char* name, int dflt) {
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
-  Choice ch{dg::kCfg128x128, 1};
+  Choice ch{dg::kCfg128x128, 1, 0};
   const int KB = K / 128;
-  if (mode == dg::kDense && rows <= 64) {
-    // decode: 64x64 tiles; split K so that every split's K blocks fit the
-    // 8-slot ring (all of them in flight at once) and the workgroups fill the chip
-    ch.cfg = dg::kCfg64x64;
+  if (mode == dg::kDense && rows <= 64 && KB > 0) {
+    // decode: 64x64 tiles; split K so that the workgroups fill the chip while
+    // each split keeps at most 8 K blocks, all of them in flight at once
+    ch.cfg = dg::kCfgDecode;
     const int tiles = ((rows + 63) / 64) * ((N + 63) / 64);
     int splits = (KB + 7) / 8;
-    while (splits < KB && tiles * (splits + 1) <= num_cus && (KB + splits) / (splits + 1) >= 4) ++splits;
-    ch.splits = splits < 1 ? 1 : splits;
+    const int fill = num_cus / (tiles > 0 ? tiles : 1);
+    if (fill > splits) splits = fill < KB ? fill : KB;
+    ch.splits = splits;
   }
   (void)groups;
   const int forced = env_int("DG_FORCE_CONFIG", -1);
-  if (forced >= 0 && forced < dg::kNumConfigs) ch.cfg = forced;
-  const int fs = env_int("DG_FORCE_SPLITS", 0);
-  if (fs > 0 && mode != dg::kMasked) ch.splits = fs;
+  if (forced >= 0 && forced < dg::kNumConfigs && (forced != dg::kCfgDecode || mode == dg::kDense)) ch.cfg = forced;
+  if (ch.cfg == dg::kCfgDecode) {
+    const int fs = env_int("DG_FORCE_SPLITS", 0);
+    if (fs > 0) ch.splits = fs;
+    if (ch.splits < (KB + 7) / 8) ch.splits = (KB + 7) / 8;   // at most 8 K blocks per split
+    if (ch.splits > KB) ch.splits = KB > 0 ? KB : 1;
+    ch.kbs = (KB + ch.splits - 1) / ch.splits;
+    ch.splits = ch.kbs > 0 ? (KB + ch.kbs - 1) / ch.kbs : 1;  // no empty splits
+  } else {
+    ch.splits = 1;
+  }
   return ch;
 }
 
@@ -127,19 +138,19 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   if (s != DG_OK) return s;
   Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
-  const int KB = p.K / 128;
-  if (ch.splits > KB && KB > 0) ch.splits = KB;
-  if (ch.splits < 1 || KB == 0) ch.splits = 1;
   p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
   p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
-  if (ch.splits > 1) {
-    const long long tiles = (long long)p.tiles_m * p.tiles_n;
-    const long long need = tiles * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
-    if (tiles > kMaxCounters || need > (long long)kWorkspaceBytes) ch.splits = 1;
-  }
   p.splits = ch.splits;
+  p.kbs_per_split = ch.kbs;
   p.workspace = st->workspace;
+  p.workspace_bytes = kWorkspaceBytes;
   p.counters = st->counters;
+  p.splitk_inline = env_int("DG_SPLITK_INLINE", 0) ? 1 : 0;
+  if (ch.splits > 1) {
+    const long long need = (long long)p.tiles_m * p.tiles_n * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
+    if (need > (long long)kWorkspaceBytes || (long long)p.tiles_m * p.tiles_n > kMaxCounters)
+      return fail(DG_ERR_UNSUPPORTED, "split-K workspace of %lld bytes exceeds %zu", need, kWorkspaceBytes);
+  }
   long long items;
   if (mode == dg::kMasked) {
     items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
@@ -151,8 +162,8 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   if (items > (1LL << 30)) return fail(DG_ERR_UNSUPPORTED, "problem too large (%lld work items)", items);
   const int grid = (int)(((items + 7) / 8) * 8);
   if (env_int("DG_LOG", 0))
-    std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d grid=%d\n", mode, p.rows, p.N,
-                 p.K, p.G, ci.name, p.splits, grid);
+    std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d kbs=%d grid=%d\n", mode, p.rows,
+                 p.N, p.K, p.G, ci.name, p.splits, p.kbs_per_split, grid);
   hipError_t e = dg::launch_gemm(mode, ch.cfg, p, grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return DG_OK;

@@ -20,20 +20,23 @@ struct Params {
   const int32_t* layout;   // contiguous: expert id per row
   const int32_t* masked_m; // masked: valid rows per group
   float* workspace;        // split-K partial tiles (fp32)
-  int32_t* counters;       // split-K arrival counters, one per output tile, kept at zero between calls
+  size_t workspace_bytes;
+  int32_t* counters;       // split-K arrivals per output tile, zero between calls
+  int splitk_inline;       // 1: the last split reduces in the GEMM kernel; 0: separate reduction kernel
   int rows;                // dense/contiguous: M; masked: max_m
   int N;
   int K;
   int G;                   // groups (1 for dense)
   int tiles_m;             // ceil(rows / BM)
   int tiles_n;             // ceil(N / BN)
-  int splits;              // split-K factor (>= 1)
+  int splits;              // split-K factor (>= 1; decode kernel only)
+  int kbs_per_split;       // K blocks per split (decode kernel only)
 };
 
 // Tile configurations compiled into the library.
 enum Config : int {
   kCfg128x128 = 0,   // 128x128 tile, 4 waves of 64x64, 4-slot ring: large GEMMs
-  kCfg64x64 = 1,     // 64x64 tile, 4 waves of 64x16, 8-slot ring: decode shapes with split-K
+  kCfgDecode = 1,    // dense only: 64x64 tile, K split over workgroups (<= 8 blocks each) and waves
   kCfg128x64 = 2,    // 128x64 tile, 4 waves of 64x32, 4-slot ring
   kCfg64x128 = 3,    // 64x128 tile, 4 waves of 64x32, 6-slot ring
   kNumConfigs
@@ -46,9 +49,10 @@ struct ConfigInfo {
 
 const ConfigInfo& config_info(int cfg);
 
-// Enqueues the kernel for `mode` with configuration `cfg` on `stream`.
-// `grid` is the number of workgroups; the kernels walk tiles (persistently
-// when grid is smaller than the tile count).
+// Enqueues the kernel(s) for `mode` with configuration `cfg` on `stream`.
+// `grid` is the number of workgroups of the tile kernel, which walks its tiles
+// persistently when grid is smaller than the tile count; the decode
+// configuration sizes its own grid from tiles and splits.
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
 
 }  // namespace dg

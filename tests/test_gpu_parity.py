@@ -145,6 +145,34 @@ def test_dense_split_k_forced_matches(dg, monkeypatch):
     monkeypatch.delenv("DG_FORCE_SPLITS")
 
 
+@pytest.mark.parametrize("reduction", ["inline", "kernel"])
+def test_decode_split_k_reductions_exact(dg, monkeypatch, reduction):
+    log(f"case: decode split-K, {reduction} reduction")
+    monkeypatch.setenv("DG_SPLITK_INLINE", "1" if reduction == "inline" else "0")
+    for M, N, K in [(64, 2112, 7168), (17, 200, 2048), (100, 640, 4096)]:
+        p = inputgen.exact_dense(M, N, K, seed=M + K)
+        ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+        for splits in ["0", "5", "8"]:
+            monkeypatch.setenv("DG_FORCE_SPLITS", splits)
+            got = run_dense(dg, p)
+            assert np.array_equal(got, ref), (M, N, K, splits)
+    monkeypatch.delenv("DG_FORCE_SPLITS")
+
+
+def test_decode_split_k_no_stale_partials(dg):
+    log("case: decode split-K, alternating inputs on one workspace")
+    probs = [inputgen.exact_dense(64, 2112, 7168, seed=s) for s in (40, 41, 42)]
+    refs = [oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c) for p in probs]
+    devs = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
+    outs = [sentinel_like((64, 2112)) for _ in probs]
+    for rep in range(4):
+        for i in range(3):
+            dg.dg_fp8_gemm_nt(*devs[i], outs[i])
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
+
+
 @pytest.mark.parametrize("cfg", ["0", "1", "2", "3"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
