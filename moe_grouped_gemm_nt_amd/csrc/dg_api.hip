@@ -4,7 +4,7 @@
 // Configuration choice (the pages' host heuristics pick a kernel layout and
 // launch shape per problem; prefill and decode shapes get different kernels,
 // zwt0204 DeepGEMM deep dive, "它的核心思路" point 2): large problems take the
-// MFMA-oriented 128x128 tile; dense decode shapes whose tile count cannot fill
+// MFMA-oriented 128x128 tile, two workgroups per CU; dense decode shapes whose tile count cannot fill
 // the 256 compute units take the 64x64 tile with K split across workgroups, so
 // that enough workgroups stream B from HBM at once, followed by a split-K
 // reduction kernel.
@@ -104,7 +104,7 @@ int env_int(const char* name, int dflt) {
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
-  Choice ch{dg::kCfg128x128, 1, 0};
+  Choice ch{dg::kCfg128x128x2, 1, 0};
   const int KB = K / 128;
   if (mode == dg::kDense && rows <= 64 && KB > 0) {
     // decode: 64x64 tiles; split K so that the workgroups fill the chip while
@@ -118,7 +118,9 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   }
   (void)groups;
   const int forced = env_int("DG_FORCE_CONFIG", -1);
-  if (forced >= 0 && forced < dg::kNumConfigs && (forced != dg::kCfgDecode || mode == dg::kDense)) ch.cfg = forced;
+  if (forced >= 0 && forced < dg::kNumConfigs && (forced != dg::kCfgDecode || mode == dg::kDense) &&
+      (mode != dg::kContiguous || dg::config_info(forced).bm <= 128))
+    ch.cfg = forced;
   if (ch.cfg == dg::kCfgDecode) {
     const int fs = env_int("DG_FORCE_SPLITS", 0);
     if (fs > 0) ch.splits = fs;

@@ -38,7 +38,10 @@ enum Config : int {
   kCfg128x128 = 0,   // 128x128 tile, 4 waves of 64x64, 4-slot ring: large GEMMs
   kCfgDecode = 1,    // dense only: 64x64 tile, K split over workgroups (<= 8 blocks each) and waves
   kCfg128x64 = 2,    // 128x64 tile, 4 waves of 64x32, 4-slot ring
-  kCfg64x128 = 3,    // 64x128 tile, 4 waves of 64x32, 6-slot ring
+  kCfg64x128 = 3,    // 64x128 tile, 4 waves of 64x32, 4-slot ring
+  kCfg128x128x2 = 4, // 128x128 tile, 2-slot ring, two workgroups per CU
+  kCfg256x128w8 = 5, // 256x128 tile, 8 waves of 64x64, 3-slot ring
+  kCfg128x256w8 = 6, // 128x256 tile, 8 waves of 64x64, 3-slot ring
   kNumConfigs
 };
 

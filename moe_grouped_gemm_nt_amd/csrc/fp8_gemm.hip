@@ -51,6 +51,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dg_internal.h"
 
 namespace dg {
@@ -184,37 +186,73 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
   nt = in_band / gm;
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
 // ============================================================================
 // prefill / grouped kernel
 // ============================================================================
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
 struct Shape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * 64;
   static constexpr int WTM = BM / WAVES_M;      // wave tile rows
   static constexpr int WTN = BN / WAVES_N;      // wave tile cols
   static constexpr int SM = WTM / 16;           // 16-row strips per wave
   static constexpr int SN = WTN / 16;           // 16-col strips per wave
-  static constexpr int A_BYTES = BM * KBLK;
+  static constexpr int A_BYTES = BM * KBLK;     // one slot of each region
   static constexpr int B_BYTES = BN * KBLK;
-  static constexpr int SA_OFF = A_BYTES + B_BYTES;
-  static constexpr int SA_PER_WAVE = BM / 4 + 4;      // BM/4 row scales, this wave's B scale, pad
-  static constexpr int SLOT = A_BYTES + B_BYTES + NWAVES * SA_PER_WAVE * 4;
+  static constexpr int RS = BM / NWAVES;        // row scales loaded per wave
+  static constexpr int SA_PER_WAVE = RS + 4;    // RS row scales, this wave's B scale, pad
+  static constexpr int S_BYTES = NWAVES * SA_PER_WAVE * 4;
+  // LDS: [A slot 0..NSLOT-1][B slot 0..NSLOT-1][scales slot 0..NSLOT-1]
+  static constexpr int B_REGION = NSLOT * A_BYTES;
+  static constexpr int S_REGION = NSLOT * (A_BYTES + B_BYTES);
+  static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
   static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
   static constexpr int B_INSTR = BN / 8 / NWAVES;
   static constexpr int LPS = A_INSTR + B_INSTR + 1;   // loads per wave per K block
-  static_assert(NWAVES == 4, "four waves per workgroup");
+  static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves per workgroup");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must sit in one 128-wide B scale block");
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "every wave issues the same number of loads");
-  static_assert(BM <= 128, "row scales plus the B scale fit one 64-lane load per wave");
+  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "every wave issues the same number of loads");
+  static_assert(RS % 4 == 0 && RS < 64, "row scales plus the B scale fit one 64-lane load per wave");
   static_assert((NSLOT - 1) * LPS < 64, "outstanding loads must fit the 6-bit vmcnt");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE>
-__global__ void __launch_bounds__(256)
+// LDS accesses at an integer LDS byte address; an added constant folds into
+// the instruction's offset field.
+__device__ __forceinline__ v4i lds_v4i(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ v4f lds_v4f(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) v4f*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
+}
+
+// Direct global->LDS load with a uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset.
+__device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WG_PER_CU)
 fp8_gemm_nt_kernel(Params p) {
   using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSLOT * S::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
   __shared__ int s_prefix[MODE == kMasked ? MAX_GROUPS_LDS + 1 : 1];
   __shared__ int s_flag;
 
@@ -226,6 +264,28 @@ fp8_gemm_nt_kernel(Params p) {
   const int wn = wave % WAVES_N;
   const int KB = p.K / KBLK;
   const int NB = (p.N + 127) / 128;
+  const int g16 = lane >> 4;          // K slice of the operands, row quad of the result
+  const int r16 = lane & 15;          // row of A / column of B within a 16-strip
+  const int wrow0 = wm * S::WTM;      // wave's first row in the tile
+  const int wcol0 = wn * S::WTN;
+
+  // per-lane LDS addresses of the fragments in slot 0 (other slots add a constant)
+  uint32_t offA[S::SM][2], offB[S::SN][2], offS[S::SM];
+#pragma unroll
+  for (int i = 0; i < S::SM; ++i) {
+    const int r = wrow0 + i * 16 + r16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) offA[i][h] = smem_base + r * KBLK + (((2 * g16 + h) ^ swz(r)) << 4);
+    const int q = wrow0 + i * 16 + g16 * 4;     // a 4-row group never straddles a wave block
+    offS[i] = smem_base + S::S_REGION + 4 * ((q / S::RS) * S::SA_PER_WAVE + q % S::RS);
+  }
+#pragma unroll
+  for (int j = 0; j < S::SN; ++j) {
+    const int r = wcol0 + j * 16 + r16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) offB[j][h] = smem_base + S::B_REGION + r * KBLK + (((2 * g16 + h) ^ swz(r)) << 4);
+  }
+  const uint32_t offSB = smem_base + S::S_REGION + 4 * (wave * S::SA_PER_WAVE + S::RS);
 
   // ---- the work list ------------------------------------------------------
   int total;
@@ -311,39 +371,35 @@ fp8_gemm_nt_kernel(Params p) {
       B += (size_t)group * p.N * p.K;
       SB += (size_t)group * NB * KB;
     }
-
-    const int wrow0 = wm * S::WTM;      // wave's first row in the tile
-    const int wcol0 = wn * S::WTN;
     int nb = (n0 + wcol0) / 128;
     nb = nb < NB ? nb : NB - 1;
 
-    // ---- per-lane load addresses (K block 0) ---------------------------------
-    // A / B: wave instruction j covers tile rows 8*(wave + 4*j) .. +7; lane l lands
+    // ---- load addresses -------------------------------------------------------
+    // A / B: wave instruction j covers tile rows 8*(wave + NWAVES*j) .. +7; lane l lands
     // at LDS byte 16*l of that 1 KB piece: row 8*(...) + l/8, physical chunk l%8,
-    // which holds logical chunk (l%8) ^ swz(row).
-    const uint8_t* a_src[S::A_INSTR];
-    const uint8_t* b_src[S::B_INSTR];
+    // which holds logical chunk (l%8) ^ swz(row).  Uniform bases (tile origin,
+    // K block) live in SGPRs; lanes add a 32-bit offset inside the tile.
+    const uint8_t* a_tile = A + (size_t)m0 * p.K;
+    const uint8_t* b_tile = B + (size_t)n0 * p.K;
+    uint32_t a_off[S::A_INSTR], b_off[S::B_INSTR];
 #pragma unroll
     for (int j = 0; j < S::A_INSTR; ++j) {
-      const int r = (wave + 4 * j) * 8 + (lane >> 3);
-      int grow = m0 + r;
-      grow = grow < a_rows ? grow : a_rows - 1;       // rows past the end are never stored
-      a_src[j] = A + (size_t)grow * p.K + (((lane & 7) ^ swz(r)) << 4);
+      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+      const int grow = min(m0 + r, a_rows - 1);       // rows past the end are never stored
+      a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < S::B_INSTR; ++j) {
-      const int r = (wave + 4 * j) * 8 + (lane >> 3);
-      int gn = n0 + r;
-      gn = gn < p.N ? gn : p.N - 1;
-      b_src[j] = B + (size_t)gn * p.K + (((lane & 7) ^ swz(r)) << 4);
+      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+      const int gn = min(n0 + r, p.N - 1);
+      b_off[j] = (uint32_t)((gn - n0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
     }
-    // scales: lanes < BM/4 load row scales of rows wave*BM/4 + lane, lane BM/4 loads
+    // scales: lanes < RS load row scales of rows wave*RS + lane, lane RS loads
     // this wave's B scale
     const float* s_src;
     size_t s_stride;                  // elements per K block
-    if (lane < BM / 4) {
-      int grow = m0 + wave * (BM / 4) + lane;
-      grow = grow < a_rows ? grow : a_rows - 1;
+    if (lane < S::RS) {
+      const int grow = min(m0 + wave * S::RS + lane, a_rows - 1);
       s_src = SA + grow;
       s_stride = a_rows;
     } else {
@@ -351,16 +407,18 @@ fp8_gemm_nt_kernel(Params p) {
       s_stride = 1;
     }
 
-    auto issue = [&](int i) {       // i: K block index
-      const uint32_t slot = smem_base + (uint32_t)((i % NSLOT) * S::SLOT);
+    // issue K block i into slot u
+    auto issue = [&](int i, int u) {
+      const uint8_t* abase = a_tile + (size_t)i * KBLK;
+      const uint8_t* bbase = b_tile + (size_t)i * KBLK;
 #pragma unroll
       for (int j = 0; j < S::A_INSTR; ++j)
-        dma_16(a_src[j] + (size_t)i * KBLK, slot + (wave + 4 * j) * 1024);
+        dma_16s(abase, a_off[j], smem_base + u * S::A_BYTES + (wave + S::NWAVES * j) * 1024);
 #pragma unroll
       for (int j = 0; j < S::B_INSTR; ++j)
-        dma_16(b_src[j] + (size_t)i * KBLK, slot + S::A_BYTES + (wave + 4 * j) * 1024);
-      if (lane <= BM / 4)
-        dma_4(s_src + (size_t)i * s_stride, slot + S::SA_OFF + wave * S::SA_PER_WAVE * 4);
+        dma_16s(bbase, b_off[j], smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
+      if (lane <= S::RS)
+        dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + wave * S::SA_PER_WAVE * 4);
     };
 
     v4f acc[S::SM][S::SN];
@@ -369,36 +427,72 @@ fp8_gemm_nt_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < S::SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    const int g16 = lane >> 4;          // row quad of the result
-
-    // ---- K loop over the slot ring -----------------------------------------------
-    const bool wraps = kbs > NSLOT;
-    const int pre = wraps ? NSLOT - 1 : kbs;
-    for (int i = 0; i < pre; ++i) issue(i);
-    for (int i = 0; i < kbs; ++i) {
-      // loads issued after block i that may stay in flight
-      const int after = min(kbs - 1 - i, wraps ? NSLOT - 2 : NSLOT - 1);
-      wait_stages<S::LPS, NSLOT - 1>(after);
-      bare_barrier();
-      if (wraps && i + NSLOT - 1 < kbs) issue(i + NSLOT - 1);
-
-      const uint8_t* base = smem + (i % NSLOT) * S::SLOT;
-      const float* sreg = reinterpret_cast<const float*>(base + S::SA_OFF);
-      const float sb = sreg[wave * S::SA_PER_WAVE + BM / 4];
+    // one K block from slot u (compile-time): fragments, promotion factors, MFMAs
+    auto compute = [&](auto u_const) {
+      constexpr int u = decltype(u_const)::value;
+      const float sb = lds_f32(offSB + u * S::S_BYTES);
+      v8i bf[S::SN], af[S::SM];
       v4f sc[S::SM];
 #pragma unroll
-      for (int ii = 0; ii < S::SM; ++ii) {
-        // scales of this lane's four result rows (a 4-row group never straddles a wave block)
-        const int q = wrow0 + ii * 16 + g16 * 4;
-        const v4f sa4 = *reinterpret_cast<const v4f*>(sreg + (q / (BM / 4)) * S::SA_PER_WAVE + q % (BM / 4));
-        sc[ii] = sa4 * sb;
+      for (int j = 0; j < S::SN; ++j) {
+        const v4i lo = lds_v4i(offB[j][0] + u * S::B_BYTES);
+        const v4i hi = lds_v4i(offB[j][1] + u * S::B_BYTES);
+        bf[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
-      mma_block<S::SM, S::SN>(base, wrow0, base + S::A_BYTES, wcol0, sc, acc, lane);
+#pragma unroll
+      for (int i = 0; i < S::SM; ++i) {
+        const v4i lo = lds_v4i(offA[i][0] + u * S::A_BYTES);
+        const v4i hi = lds_v4i(offA[i][1] + u * S::A_BYTES);
+        af[i] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sc[i] = lds_v4f(offS[i] + u * S::S_BYTES) * sb;
+      }
+      constexpr int T = S::SM * S::SN;
+      constexpr int P = 4;
+      v4f part[P];
+#pragma unroll
+      for (int t = 0; t < T + P - 1; ++t) {
+        if (t < T) {
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
+                                                                         0, 0, 0, 0, 0, 0);
+        }
+        const int v = t - (P - 1);
+        if (v >= 0) {
+          v4f& a = acc[v / S::SN][v % S::SN];
+          const v4f& q = part[v % P];
+          const v4f& c = sc[v / S::SN];
+          a.x = __builtin_fmaf(q.x, c.x, a.x);
+          a.y = __builtin_fmaf(q.y, c.y, a.y);
+          a.z = __builtin_fmaf(q.z, c.z, a.z);
+          a.w = __builtin_fmaf(q.w, c.w, a.w);
+        }
+      }
+    };
+
+    // ---- K loop over the slot ring, unrolled by NSLOT so slots are constants --
+    const bool wraps = kbs > NSLOT;
+    const int pre = wraps ? NSLOT - 1 : kbs;
+#pragma unroll
+    for (int u = 0; u < NSLOT - 1; ++u)
+      if (u < pre) issue(u, u);
+    if (!wraps && kbs == NSLOT) issue(NSLOT - 1, NSLOT - 1);
+    for (int i0 = 0; i0 < kbs; i0 += NSLOT) {
+      static_for<NSLOT>([&](auto u_const) {
+        constexpr int u = decltype(u_const)::value;
+        const int i = i0 + u;
+        if (i < kbs) {
+          // loads issued after block i that may stay in flight
+          const int after = min(kbs - 1 - i, wraps ? NSLOT - 2 : NSLOT - 1);
+          wait_stages<S::LPS, NSLOT - 1>(after);
+          bare_barrier();
+          if (wraps && i + NSLOT - 1 < kbs) issue(i + NSLOT - 1, (u + NSLOT - 1) % NSLOT);
+          compute(u_const);
+        }
+      });
     }
 
     // ---- epilogue: + C, round to bf16, store the rows that belong to the result
     // All loads (row ids, C) are issued before any store so their latencies overlap.
-    const int r16 = lane & 15;
     bool row_ok[S::SM][4];
 #pragma unroll
     for (int i = 0; i < S::SM; ++i)
@@ -691,19 +785,19 @@ splitk_reduce_kernel(Params p) {
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU = 1>
 hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
   switch (mode) {
     case kDense:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense>), dim3(grid), dim3(256), 0,
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense, WG_PER_CU>), dim3(grid), dim3(WAVES_M * WAVES_N * 64), 0,
                          stream, p);
       break;
     case kContiguous:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kContiguous>), dim3(grid), dim3(256),
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kContiguous, WG_PER_CU>), dim3(grid), dim3(WAVES_M * WAVES_N * 64),
                          0, stream, p);
       break;
     case kMasked:
-      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kMasked>), dim3(grid), dim3(256), 0,
+      hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kMasked, WG_PER_CU>), dim3(grid), dim3(WAVES_M * WAVES_N * 64), 0,
                          stream, p);
       break;
     default:
@@ -726,7 +820,10 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     {128, 128, 256, "128x128_w2x2_s4"},
     {DBM, DBN, 256, "decode_64x64_ksplit"},
     {128, 64, 256, "128x64_w2x2_s4"},
-    {64, 128, 256, "64x128_w1x4_s6"},
+    {64, 128, 256, "64x128_w1x4_s4"},
+    {128, 128, 256, "128x128_w2x2_s2_2wg"},
+    {256, 128, 512, "256x128_w4x2_s3"},
+    {128, 256, 512, "128x256_w2x4_s3"},
 };
 
 }  // namespace
@@ -738,7 +835,10 @@ hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t
     case kCfg128x128: return launch_cfg<128, 128, 2, 2, 4>(mode, p, grid, stream);
     case kCfgDecode: return mode == kDense ? launch_decode(p, stream) : hipErrorInvalidValue;
     case kCfg128x64: return launch_cfg<128, 64, 2, 2, 4>(mode, p, grid, stream);
-    case kCfg64x128: return launch_cfg<64, 128, 1, 4, 6>(mode, p, grid, stream);
+    case kCfg64x128: return launch_cfg<64, 128, 1, 4, 4>(mode, p, grid, stream);
+    case kCfg128x128x2: return launch_cfg<128, 128, 2, 2, 2, 2>(mode, p, grid, stream);
+    case kCfg256x128w8: return launch_cfg<256, 128, 4, 2, 3>(mode, p, grid, stream);
+    case kCfg128x256w8: return launch_cfg<128, 256, 2, 4, 3>(mode, p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -173,7 +173,7 @@ def test_decode_split_k_no_stale_partials(dg):
             assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
 
 
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -223,6 +223,52 @@ def test_contiguous_small_random(dg):
     ref, written = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.grouped_layout)
     assert written.all()
     check_tolerance(got, ref, "contiguous small")
+
+
+@pytest.mark.parametrize("cfg", ["0", "2", "3", "4", "5", "6"])
+def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
+    log(f"case: contiguous exact, forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    G, N, K = 3, 384, 768
+    counts = np.array([200, 5, 300])
+    segs = [((c + 127) // 128) * 128 for c in counts]
+    M = sum(segs)
+    layout = np.full(M, -1, dtype=np.int32)
+    off = 0
+    for g, (cnt, sg) in enumerate(zip(counts, segs)):
+        layout[off:off + cnt] = g
+        off += sg
+    base = inputgen.exact_dense(M, N, K, seed=9)
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=60 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=70 + g).sfb for g in range(G)])
+    d = sentinel_like((M, N))
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(base.a), dev(base.sfa), dev(b), dev(sfb),
+                                           bf16_bits_dev(base.c), d, dev(layout))
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_contiguous(base.a, base.sfa, b, sfb, layout, base.c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
+
+
+@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6"])
+def test_masked_every_tile_config_exact(dg, monkeypatch, cfg):
+    log(f"case: masked exact, forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    G, max_m, N, K = 5, 320, 256, 512
+    base = inputgen.exact_dense(G * max_m, N, K, seed=33)
+    a = base.a.reshape(G, max_m, K)
+    sfa = np.ascontiguousarray(base.sfa.reshape(K // 128, G, max_m).transpose(1, 0, 2))
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=80 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=90 + g).sfb for g in range(G)])
+    masked_m = np.array([320, 0, 1, 129, 257], dtype=np.int32)
+    d = sentinel_like((G, max_m, N))
+    dg.dg_m_grouped_fp8_gemm_nt_masked(dev(a), dev(sfa), dev(b), dev(sfb), None, d, dev(masked_m), 128)
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_masked(a, sfa, b, sfb, masked_m)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
 
 
 def test_contiguous_exact_with_padding_ids_and_empty_expert(dg):
