@@ -14,15 +14,20 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdg.so")
-SOURCES = ["fp8_gemm.hip", "dg_api.hip"]
+# source -> extra flags.  The fp32-promotion kernels want MFMA results in
+# VGPRs, where the promotion FMAs read them; the power-of-two-scale kernels
+# keep their accumulators in AGPRs.
+SOURCES = {
+    "fp8_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "fp8_gemm_e8m0.hip": [],
+    "dg_api.hip": [],
+}
 
-# packed fp32 VALU forms are disabled on purpose (see the design notes);
-# MFMA results go straight to VGPRs, where the fp32 promotion reads them
+# packed fp32 VALU forms are disabled on purpose (see the design notes)
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 
@@ -33,10 +38,7 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-I", INCLUDE, "-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,6 +49,19 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src, flags in SOURCES.items():
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        _run([hipcc()] + HIPCC_FLAGS + flags + list(extra_flags or []) +
+             ["-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

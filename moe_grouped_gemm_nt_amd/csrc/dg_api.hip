@@ -3,11 +3,17 @@
 //
 // Configuration choice (the pages' host heuristics pick a kernel layout and
 // launch shape per problem; prefill and decode shapes get different kernels,
-// zwt0204 DeepGEMM deep dive, "它的核心思路" point 2): large problems take the
-// MFMA-oriented 128x128 tile, two workgroups per CU; dense decode shapes whose tile count cannot fill
-// the 256 compute units take the 64x64 tile with K split across workgroups, so
-// that enough workgroups stream B from HBM at once, followed by a split-K
-// reduction kernel.
+// zwt0204 DeepGEMM deep dive, "它的核心思路" point 2):
+//   * dense decode shapes (at most 64 rows) take the 64x64 tile with K split
+//     across workgroups, so that enough workgroups stream B from HBM at once,
+//     followed by a split-K reduction kernel;
+//   * large problems enqueue three kernels: a scale check, the power-of-two
+//     kernel (128x256 tiles, scales applied inside the MFMA, loads issued by
+//     dedicated waves) and the general
+//     kernel (128x128 tiles, two workgroups per CU, fp32 promotion); the check
+//     leaves verdicts on the device and exactly one of the two GEMM kernels
+//     does the work, so no host synchronisation is needed;
+//   * the rest take the general kernel alone.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -44,6 +50,7 @@ struct DeviceState {
   int num_cus = 0;
   float* workspace = nullptr;
   int32_t* counters = nullptr;
+  int32_t* verdicts = nullptr;    // scale check results, dg::kCheckWGs entries
 };
 
 DeviceState g_dev[kMaxDevices];
@@ -68,6 +75,8 @@ int get_device_state(DeviceState** out) {
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace): %s", hipGetErrorString(e));
       e = hipMalloc(&st.counters, sizeof(int32_t) * kMaxCounters);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(counters): %s", hipGetErrorString(e));
+      e = hipMalloc(&st.verdicts, sizeof(int32_t) * dg::kCheckWGs);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(verdicts): %s", hipGetErrorString(e));
       e = hipMemset(st.counters, 0, sizeof(int32_t) * kMaxCounters);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) return fail(DG_ERR_HIP, "clearing split-K counters: %s", hipGetErrorString(e));
@@ -94,7 +103,8 @@ int check_common(const void* a, const float* sfa, const void* b, const float* sf
 struct Choice {
   int cfg;
   int splits;
-  int kbs;      // K blocks per split (decode configuration)
+  int kbs;        // K blocks per split (decode configuration)
+  int gated_cfg;  // >= 0: power-of-two kernel run beside cfg behind the scale check
 };
 
 int env_int(const char* name, int dflt) {
@@ -102,9 +112,13 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
+// Problems of at least this many multiply-adds take the gated pair; below it
+// the two extra launches would cost more than the faster kernel saves.
+constexpr double kGateMinMacs = 2.0e9;
+
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
-  Choice ch{dg::kCfg128x128x2, 1, 0};
+  Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const int KB = K / 128;
   if (mode == dg::kDense && rows <= 64 && KB > 0) {
     // decode: 64x64 tiles; split K so that the workgroups fill the chip while
@@ -115,12 +129,23 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
     const int fill = num_cus / (tiles > 0 ? tiles : 1);
     if (fill > splits) splits = fill < KB ? fill : KB;
     ch.splits = splits;
+  } else if ((double)rows * N * K * (mode == dg::kMasked ? groups : 1) >= kGateMinMacs) {
+    ch.gated_cfg = dg::kCfgWs_128x256;
   }
-  (void)groups;
+  // DG_FORCE_CONFIG picks a configuration (a power-of-two one runs gated beside
+  // the default general one); DG_SCALE_PATH=1 turns the gated pair off.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced >= 0 && forced < dg::kNumConfigs && (forced != dg::kCfgDecode || mode == dg::kDense) &&
-      (mode != dg::kContiguous || dg::config_info(forced).bm <= 128))
-    ch.cfg = forced;
+      (mode != dg::kContiguous || dg::config_info(forced).bm <= 128)) {
+    if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256) {
+      ch.cfg = dg::kCfg128x128x2;
+      ch.gated_cfg = forced;
+    } else {
+      ch.cfg = forced;
+      ch.gated_cfg = -1;
+    }
+  }
+  if (env_int("DG_SCALE_PATH", 0) == 1 || ch.cfg == dg::kCfgDecode) ch.gated_cfg = -1;
   if (ch.cfg == dg::kCfgDecode) {
     const int fs = env_int("DG_FORCE_SPLITS", 0);
     if (fs > 0) ch.splits = fs;
@@ -134,39 +159,71 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   return ch;
 }
 
+// Fills the tile counts of p for configuration cfg and returns its grid (0 on
+// error).  The tile kernels walk their work list persistently: masked grids,
+// and both grids of a gated pair (one of which exits at once), hold only as
+// many workgroups as are resident on the chip together.
+int plan(int mode, int cfg, dg::Params& p, const DeviceState* st, bool gated) {
+  const dg::ConfigInfo& ci = dg::config_info(cfg);
+  p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
+  p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
+  long long items;
+  const long long resident = (long long)st->num_cus * (ci.bm * ci.bn <= 128 * 128 ? 2 : 1);
+  if (mode == dg::kMasked) {
+    items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
+    if (items > resident) items = resident;
+  } else {
+    items = (long long)p.tiles_m * p.tiles_n * p.splits;
+    if (gated && items > resident) items = resident;
+  }
+  if (items > (1LL << 30)) {
+    fail(DG_ERR_UNSUPPORTED, "problem too large (%lld work items)", items);
+    return 0;
+  }
+  return (int)(((items + 7) / 8) * 8);
+}
+
 int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   DeviceState* st = nullptr;
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
+  if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
   Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
-  p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
-  p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
   p.workspace = st->workspace;
   p.workspace_bytes = kWorkspaceBytes;
   p.counters = st->counters;
   p.splitk_inline = env_int("DG_SPLITK_INLINE", 0) ? 1 : 0;
+  p.gate_ok = nullptr;
+  const int grid = plan(mode, ch.cfg, p, st, ch.gated_cfg >= 0);
+  if (grid == 0) return DG_ERR_UNSUPPORTED;
   if (ch.splits > 1) {
     const long long need = (long long)p.tiles_m * p.tiles_n * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
     if (need > (long long)kWorkspaceBytes || (long long)p.tiles_m * p.tiles_n > kMaxCounters)
       return fail(DG_ERR_UNSUPPORTED, "split-K workspace of %lld bytes exceeds %zu", need, kWorkspaceBytes);
   }
-  long long items;
-  if (mode == dg::kMasked) {
-    items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
-    const long long cap = (long long)st->num_cus * 2;
-    if (items > cap) items = cap;
-  } else {
-    items = (long long)p.tiles_m * p.tiles_n * p.splits;
-  }
-  if (items > (1LL << 30)) return fail(DG_ERR_UNSUPPORTED, "problem too large (%lld work items)", items);
-  const int grid = (int)(((items + 7) / 8) * 8);
-  if (env_int("DG_LOG", 0))
+  hipError_t e = hipSuccess;
+  if (ch.gated_cfg >= 0) {
+    dg::Params pe = p;
+    const int grid_e = plan(mode, ch.gated_cfg, pe, st, true);
+    if (grid_e == 0) return DG_ERR_UNSUPPORTED;
+    const int KB = p.K / 128;
+    const int NB = (p.N + 127) / 128;
+    const size_t na = (size_t)KB * p.rows * (mode == dg::kMasked ? p.G : 1);
+    const size_t nb = (size_t)NB * KB * (mode == dg::kDense ? 1 : p.G);
+    p.gate_ok = pe.gate_ok = st->verdicts;
+    if (env_int("DG_LOG", 0))
+      std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d gated cfg=%s grid=%d | cfg=%s grid=%d\n", mode,
+                   p.rows, p.N, p.K, p.G, dg::config_info(ch.gated_cfg).name, grid_e, ci.name, grid);
+    e = dg::launch_scale_check(p.sfa, na, p.sfb, nb, st->verdicts, stream);
+    if (e == hipSuccess) e = dg::launch_gemm(mode, ch.gated_cfg, pe, grid_e, stream);
+  } else if (env_int("DG_LOG", 0)) {
     std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d kbs=%d grid=%d\n", mode, p.rows,
                  p.N, p.K, p.G, ci.name, p.splits, p.kbs_per_split, grid);
-  hipError_t e = dg::launch_gemm(mode, ch.cfg, p, grid, stream);
+  }
+  if (e == hipSuccess) e = dg::launch_gemm(mode, ch.cfg, p, grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return DG_OK;
 }

@@ -23,6 +23,7 @@ struct Params {
   size_t workspace_bytes;
   int32_t* counters;       // split-K arrivals per output tile, zero between calls
   int splitk_inline;       // 1: the last split reduces in the GEMM kernel; 0: separate reduction kernel
+  const int32_t* gate_ok;  // scale check verdicts (kernel path gate), or nullptr for no gate
   int rows;                // dense/contiguous: M; masked: max_m
   int N;
   int K;
@@ -42,6 +43,8 @@ enum Config : int {
   kCfg128x128x2 = 4, // 128x128 tile, 2-slot ring, two workgroups per CU
   kCfg256x128w8 = 5, // 256x128 tile, 8 waves of 64x64, 3-slot ring
   kCfg128x256w8 = 6, // 128x256 tile, 8 waves of 64x64, 3-slot ring
+  kCfgE8_128x256 = 7, // power-of-two scales only: 128x256 tile, 4 waves of 64x128, 3-slot ring
+  kCfgWs_128x256 = 8, // power-of-two scales only: as 7 plus 4 loader waves (wave-specialised)
   kNumConfigs
 };
 
@@ -57,5 +60,16 @@ const ConfigInfo& config_info(int cfg);
 // persistently when grid is smaller than the tile count; the decode
 // configuration sizes its own grid from tiles and splits.
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
+
+// Power-of-two-scale kernels (fp8_gemm_e8m0.hip).  Launched with a gate
+// (Params::gate_ok) after launch_scale_check, beside the general kernel with
+// the same gate: exactly one of the two does the work.
+hipError_t launch_gemm_e8m0(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
+
+// Writes kCheckWGs verdicts (int32, 1 = every scale in sfa[0..na) and
+// sfb[0..nb) is a positive normal power of two).
+constexpr int kCheckWGs = 64;
+hipError_t launch_scale_check(const float* sfa, size_t na, const float* sfb, size_t nb, int32_t* verdicts,
+                              hipStream_t stream);
 
 }  // namespace dg

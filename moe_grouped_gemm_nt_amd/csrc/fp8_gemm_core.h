@@ -1,0 +1,594 @@
+// gfx950 kernels for the FP8 (e4m3) block-scaled GEMM, NT layout, and its two
+// M-grouped MoE forms.
+//
+// Computation (likun.im DeepGEMM article, section 一: D = C + A @ B in the NT
+// layout; aitangshan.cn DeepGEMM article, "4. FP8 精度优化的核心": each block's
+// GEMM result is multiplied by the block's scales): for every 128-wide K
+// block kb, one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output sub-tile forms the
+// block's partial sum in fp32 from zero; the partial is then promoted into the
+// fp32 total with one FMA per element, total += partial * (sa[kb][m] * sb[n/128][kb]).
+// After the last block, C is added and the total is rounded to bf16 (RNE).
+//
+// Two kernels share that per-block step:
+//
+// fp8_gemm_nt_kernel (prefill shapes and both grouped forms)
+//   * a workgroup of four waves owns a BM x BN output tile; each wave owns a
+//     (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in VGPRs;
+//   * A and B K-blocks travel HBM -> LDS through the direct global->LDS path
+//     (global_load_lds_dwordx4: no VGPR staging) into a ring of NSLOT slots,
+//     so up to NSLOT-1 K-blocks are in flight while one feeds the MFMAs; each
+//     wave waits only for its own loads of the block it is about to use
+//     (s_waitcnt vmcnt(n)) and a bare s_barrier publishes them; the A scales
+//     of the tile's rows and each wave's B scale ride in the same slot;
+//   * workgroups walk a list of work items; the list is split into 8
+//     contiguous ranges, one per XCD (the hardware deals workgroups to the
+//     XCDs round-robin), so that tiles sharing A rows or B columns run on the
+//     same XCD and meet in its L2;
+//   * masked form: each workgroup builds the per-group tile counts from the
+//     device-resident masked_m in LDS and walks the expert groups, skipping
+//     empty ones; contiguous form: the expert of each 128-row block is read
+//     from the device-resident grouped_layout.
+//
+// fp8_gemm_nt_decode_kernel (dense shapes with few rows)
+//   * a workgroup owns a 64x64 tile and a range of at most 8 K-blocks (a K
+//     split); its four waves split those K-blocks among themselves, each wave
+//     loading and consuming only its own blocks with no barrier in the K loop;
+//     every load of the workgroup is issued up front, so the whole range is in
+//     flight at once;
+//   * the four wave totals are summed through LDS in wave order; with one
+//     split the result goes through the +C / bf16 epilogue; otherwise every
+//     split stores its fp32 partial to a workspace and splitk_reduce_kernel,
+//     launched next on the same stream, sums the splits in split order
+//     (deterministic), adds C and rounds; the kernel boundary orders the two.
+//     An in-kernel alternative (selected on the host) lets the last split to
+//     arrive do that sum: partials go through device-scope (sc1) stores and
+//     loads, coherent across the XCDs' L2 caches without flushing or
+//     invalidating them, and a per-tile arrival counter is reset to zero by
+//     the last split for the next call.
+//
+// LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row so that the
+// fragment reads of a 16-row strip are free of bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int KBLK = 128;        // K block of the scales and of one MFMA
+
+constexpr int MAX_GROUPS_LDS = 1024;
+
+// 16-byte chunk swizzle of a 128-byte LDS row.  It depends only on the row's
+// position inside its 16-row strip, so a strip's addresses are those of strip 0
+// plus a constant, and the 16 rows read by one fragment instruction hit 8
+// distinct chunk positions in each half.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 h = static_cast<__bf16>(x);   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// s_waitcnt with vmcnt <= N and all LDS reads of this wave complete
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Runtime-selected wait: vmcnt <= n * LPS for n in [0, MAXN].
+template <int LPS, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN >= 0) {
+    if (n >= MAXN) {
+      wait_vm_lgkm0<LPS * MAXN>();
+      return;
+    }
+    wait_stages<LPS, MAXN - 1>(n);
+  }
+}
+
+// Direct global->LDS loads.  Lane l's bytes land at LDS address m0 + size*l.
+// Written as inline asm so that the compiler does not treat every later LDS
+// read as dependent on every load in flight (it cannot tell the ring slots
+// apart and would wait for all of them); the kernels wait on vmcnt themselves.
+// One wait state separates the M0 write from the load that uses it.
+__device__ __forceinline__ void dma_16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  // the C-style cast is an address-space cast: generic -> LDS offset
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)(p));
+}
+
+// barrier that does not wait for outstanding global->LDS loads; the caller has
+// already waited for the ones it needs.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Reads the MFMA operand fragment of one 16-row strip: lane l takes row l%16
+// of the strip and the 32-byte K slice l/16 of it (logical 16-byte chunks
+// 2*(l/16) and 2*(l/16)+1, stored at their swizzled positions).
+__device__ __forceinline__ v8i lds_fragment(const uint8_t* rows, int r, int g16) {
+  const uint8_t* rp = rows + r * KBLK;
+  const int s = swz(r);
+  const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * g16) ^ s) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * g16 + 1) ^ s) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// One 128-wide K block for a (16*SM) x (16*SN) wave sub-tile whose A rows
+// start at row arow0 of `a_rows` and whose B rows start at row bcol0 of
+// `b_rows` (both LDS, 128-byte swizzled rows).  sc[i] holds the promotion
+// factors sa*sb of the lane's four result rows in strip i.
+//
+// Software pipeline over the sub-tiles: the MFMA of sub-tile t is issued
+// before the promotion of sub-tile t-(P-1), so P-1 MFMAs are in flight while
+// the VALU promotes a finished partial.
+template <int SM, int SN>
+__device__ __forceinline__ void mma_block(const uint8_t* a_rows, int arow0, const uint8_t* b_rows, int bcol0,
+                                          const v4f (&sc)[SM], v4f (&acc)[SM][SN], int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  v8i bf[SN], af[SM];
+#pragma unroll
+  for (int j = 0; j < SN; ++j) bf[j] = lds_fragment(b_rows, bcol0 + j * 16 + r16, g16);
+#pragma unroll
+  for (int i = 0; i < SM; ++i) af[i] = lds_fragment(a_rows, arow0 + i * 16 + r16, g16);
+  constexpr int T = SM * SN;
+  constexpr int P = 4;
+  v4f part[P];
+#pragma unroll
+  for (int t = 0; t < T + P - 1; ++t) {
+    if (t < T) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / SN], bf[t % SN], zero, 0, 0, 0, 0, 0, 0);
+    }
+    const int u = t - (P - 1);
+    if (u >= 0) {
+      v4f& a = acc[u / SN][u % SN];
+      const v4f& q = part[u % P];
+      const v4f& c = sc[u / SN];
+      a.x = __builtin_fmaf(q.x, c.x, a.x);
+      a.y = __builtin_fmaf(q.y, c.y, a.y);
+      a.z = __builtin_fmaf(q.z, c.z, a.z);
+      a.w = __builtin_fmaf(q.w, c.w, a.w);
+    }
+  }
+}
+
+// Output tile of linear tile id `tile` in the grouped order: bands of 8
+// m-tiles sweep across n, so consecutive tiles share B columns.
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& mt, int& nt) {
+  constexpr int GM = 8;
+  const int band = tile / (GM * tiles_n);
+  const int first_m = band * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in_band = tile - band * GM * tiles_n;
+  mt = first_m + in_band % gm;
+  nt = in_band / gm;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
+// ============================================================================
+// prefill / grouped kernel
+// ============================================================================
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
+struct Shape {
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int WTM = BM / WAVES_M;      // wave tile rows
+  static constexpr int WTN = BN / WAVES_N;      // wave tile cols
+  static constexpr int SM = WTM / 16;           // 16-row strips per wave
+  static constexpr int SN = WTN / 16;           // 16-col strips per wave
+  static constexpr int A_BYTES = BM * KBLK;     // one slot of each region
+  static constexpr int B_BYTES = BN * KBLK;
+  static constexpr int RS = BM / NWAVES;        // row scales loaded per wave
+  static constexpr int SA_PER_WAVE = RS + 4;    // RS row scales, this wave's B scale, pad
+  static constexpr int S_BYTES = NWAVES * SA_PER_WAVE * 4;
+  // LDS: [A slot 0..NSLOT-1][B slot 0..NSLOT-1][scales slot 0..NSLOT-1]
+  static constexpr int B_REGION = NSLOT * A_BYTES;
+  static constexpr int S_REGION = NSLOT * (A_BYTES + B_BYTES);
+  static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
+  static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
+  static constexpr int B_INSTR = BN / 8 / NWAVES;
+  // with 64 row scales per wave the B scale needs a load of its own
+  static constexpr bool SB_SEP = RS >= 64;
+  static constexpr int LPS = A_INSTR + B_INSTR + 1 + SB_SEP;   // loads per wave per K block
+  static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves per workgroup");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must sit in one 128-wide B scale block");
+  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "every wave issues the same number of loads");
+  static_assert(RS % 4 == 0 && RS <= 64, "row scales fit one 64-lane load per wave");
+  static_assert((NSLOT - 1) * LPS < 64, "outstanding loads must fit the 6-bit vmcnt");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+  // strips start on a wave block boundary plus a multiple of 16 rows, so the scale
+  // slot of row (16*i + x), x < 16, is that of row x plus a constant
+  static_assert(WTM % RS == 0 && RS % 16 == 0, "scale addresses of strips differ by constants");
+  static constexpr int strip_scale_off(int i) { return 4 * (((16 * i) / RS) * SA_PER_WAVE + (16 * i) % RS); }
+};
+
+// LDS accesses at an integer LDS byte address; an added constant folds into
+// the instruction's offset field.
+__device__ __forceinline__ v4i lds_v4i(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ v4f lds_v4f(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) v4f*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
+}
+
+// Direct global->LDS load with a uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset.
+__device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+// E8M0 = false: MFMA partials promoted by fp32 FMAs (any scales).
+// E8M0 = true:  every scale is a power of two, applied by the MFMA itself from
+//               its E8M0 exponent; results accumulate in place (AGPRs).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU, bool E8M0>
+__global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WG_PER_CU)
+fp8_gemm_nt_kernel(Params p) {
+  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT>;
+  // Path gate: the scale check kernel leaves one verdict per check workgroup;
+  // the E8M0 kernel runs only if all scales are powers of two, the other
+  // kernel only if not.  Every lane reads the same verdicts, so the exit is
+  // uniform.
+  if (p.gate_ok) {
+    const int ok = (threadIdx.x & 63) < kCheckWGs ? p.gate_ok[threadIdx.x & 63] : 1;
+    const bool all_pow2 = __builtin_amdgcn_ballot_w64(ok == 0) == 0;
+    if (all_pow2 != E8M0) return;
+  }
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
+  __shared__ int s_prefix[MODE == kMasked ? MAX_GROUPS_LDS + 1 : 1];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t smem_base = lds_u32(smem);
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int KB = p.K / KBLK;
+  const int NB = (p.N + 127) / 128;
+  const int g16 = lane >> 4;          // K slice of the operands, row quad of the result
+  const int r16 = lane & 15;          // row of A / column of B within a 16-strip
+  const int wrow0 = wm * S::WTM;      // wave's first row in the tile
+  const int wcol0 = wn * S::WTN;
+
+  // per-lane LDS addresses of the fragments of strip 0 in slot 0; strip i and
+  // slot u add the constants 2048*i and u*region bytes (the swizzle repeats
+  // every 16 rows)
+  uint32_t offA0[2], offB0[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    offA0[h] = smem_base + (wrow0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4);
+    offB0[h] = smem_base + S::B_REGION + (wcol0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4);
+  }
+  // row scales of the lane's four result rows in strip 0 (strip i adds strip_scale_off(i))
+  const uint32_t offS0 = smem_base + S::S_REGION +
+                         4 * (((wrow0 + g16 * 4) / S::RS) * S::SA_PER_WAVE + (wrow0 + g16 * 4) % S::RS);
+  const uint32_t offSB = smem_base + S::S_REGION + 4 * (wave * S::SA_PER_WAVE + S::RS);
+  // scale of the lane's MFMA operand row (row 16*i + l%16 of the wave tile) in strip 0
+  const uint32_t offR0 = smem_base + S::S_REGION +
+                         4 * (((wrow0 + r16) / S::RS) * S::SA_PER_WAVE + (wrow0 + r16) % S::RS);
+
+  // ---- the work list ------------------------------------------------------
+  int total;
+  if constexpr (MODE == kMasked) {
+    // exclusive prefix over groups of (m tiles * n tiles); masked_m clamped to [0, max_m]
+    if (tid == 0) {
+      int acc = 0;
+      for (int g = 0; g < p.G; ++g) {
+        int m = p.masked_m[g];
+        m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
+        s_prefix[g] = acc;
+        acc += ((m + BM - 1) / BM) * p.tiles_n;
+      }
+      s_prefix[p.G] = acc;
+    }
+    __syncthreads();
+    total = s_prefix[p.G];
+  } else {
+    total = p.tiles_m * p.tiles_n;
+  }
+
+  const int slots = (gridDim.x + 7) / 8;          // workgroups per XCD
+  const int xcd = blockIdx.x % 8;
+  const int slot_id = blockIdx.x / 8;
+  const int per_xcd = (total + 7) / 8;
+  const int w_begin = xcd * per_xcd;
+  const int w_end = min(total, w_begin + per_xcd);
+  int g_cur = 0;                                   // masked walker state
+
+  for (int w = w_begin + slot_id; w < w_end; w += slots) {
+    // ---- resolve the work item ---------------------------------------------
+    int group = 0, mt, nt, rows_lim = p.rows;
+    if constexpr (MODE == kMasked) {
+      while (w >= s_prefix[g_cur + 1]) ++g_cur;
+      const int local = w - s_prefix[g_cur];
+      int m = p.masked_m[g_cur];
+      m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
+      const int tm = (m + BM - 1) / BM;
+      group = g_cur;
+      mt = local % tm;             // the m-tiles of one B tile are neighbours in the list
+      nt = local / tm;
+      rows_lim = m;
+    } else {
+      tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
+      if constexpr (MODE == kContiguous) {
+        // the expert of this block of rows: the largest id among its rows
+        // (padding rows may carry -1); all valid ids in a block agree
+        if (wave == 0) {
+          int best = -1;
+          for (int r = lane; r < BM; r += 64) {
+            const int row = mt * BM + r;
+            if (row < p.rows) best = max(best, p.layout[row]);
+          }
+          for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
+          if (lane == 0) s_flag = best;
+        }
+        __syncthreads();
+        group = s_flag;
+        __syncthreads();
+        if (group < 0 || group >= p.G) continue;   // uniform across the workgroup
+      }
+    }
+
+    const int m0 = mt * BM;
+    const int n0 = nt * BN;
+    const int kbs = KB;
+
+    // ---- operand bases -----------------------------------------------------
+    const uint8_t* A = p.a;
+    const float* SA = p.sfa;
+    const uint8_t* B = p.b;
+    const float* SB = p.sfb;
+    uint16_t* D = p.d;
+    const uint16_t* C = p.c;
+    const int a_rows = p.rows;     // rows allocated in this A operand
+    if constexpr (MODE == kMasked) {
+      A += (size_t)group * p.rows * p.K;
+      SA += (size_t)group * KB * p.rows;
+      D += (size_t)group * p.rows * p.N;
+      if (C) C += (size_t)group * p.rows * p.N;
+    }
+    if constexpr (MODE != kDense) {
+      B += (size_t)group * p.N * p.K;
+      SB += (size_t)group * NB * KB;
+    }
+    int nb = (n0 + wcol0) / 128;
+    nb = nb < NB ? nb : NB - 1;
+
+    // ---- load addresses -------------------------------------------------------
+    // A / B: wave instruction j covers tile rows 8*(wave + NWAVES*j) .. +7; lane l lands
+    // at LDS byte 16*l of that 1 KB piece: row 8*(...) + l/8, physical chunk l%8,
+    // which holds logical chunk (l%8) ^ swz(row).  Uniform bases (tile origin,
+    // K block) live in SGPRs; lanes add a 32-bit offset inside the tile.
+    const uint8_t* a_tile = A + (size_t)m0 * p.K;
+    const uint8_t* b_tile = B + (size_t)n0 * p.K;
+    uint32_t a_off[S::A_INSTR], b_off[S::B_INSTR];
+#pragma unroll
+    for (int j = 0; j < S::A_INSTR; ++j) {
+      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+      const int grow = min(m0 + r, a_rows - 1);       // rows past the end are never stored
+      a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < S::B_INSTR; ++j) {
+      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+      const int gn = min(n0 + r, p.N - 1);
+      b_off[j] = (uint32_t)((gn - n0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+    }
+    // scales: lanes < RS load row scales of rows wave*RS + lane, lane RS (or
+    // lane 0 of a separate load when RS is 64) loads this wave's B scale
+    const float* s_src;
+    size_t s_stride;                  // elements per K block
+    const float* sb_src = SB + (size_t)nb * KB;
+    if (lane < S::RS) {
+      const int grow = min(m0 + wave * S::RS + lane, a_rows - 1);
+      s_src = SA + grow;
+      s_stride = a_rows;
+    } else {
+      s_src = SB + (size_t)nb * KB;
+      s_stride = 1;
+    }
+
+    // the k-th load instruction (k < LPS) of K block i into slot u
+    auto issue_one = [&](int k, int i, int u) {
+      if (k < S::A_INSTR) {
+        dma_16s(a_tile + (size_t)i * KBLK, a_off[k], smem_base + u * S::A_BYTES + (wave + S::NWAVES * k) * 1024);
+      } else if (k < S::A_INSTR + S::B_INSTR) {
+        const int j = k - S::A_INSTR;
+        dma_16s(b_tile + (size_t)i * KBLK, b_off[j],
+                smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
+      } else if (!S::SB_SEP || k == S::A_INSTR + S::B_INSTR) {
+        if (lane <= S::RS)
+          dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + wave * S::SA_PER_WAVE * 4);
+      } else if (lane == 0) {
+        dma_4(sb_src + i, smem_base + S::S_REGION + u * S::S_BYTES + (wave * S::SA_PER_WAVE + S::RS) * 4);
+      }
+    };
+    auto issue = [&](int i, int u) {
+#pragma unroll
+      for (int k = 0; k < S::LPS; ++k) issue_one(k, i, u);
+    };
+
+    v4f acc[S::SM][S::SN];
+#pragma unroll
+    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // one K block from slot u (compile-time): fragments, promotion factors, MFMAs.
+    // The loads of block `next` into slot next_u are spread between the MFMAs so
+    // the vector-memory queue drains while the matrix cores run.
+    auto compute = [&](auto u_const, int next, int next_u) {
+      constexpr int u = decltype(u_const)::value;
+      const float sb = lds_f32(offSB + u * S::S_BYTES);
+      auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) {
+        const v4i lo = lds_v4i(lo_addr), hi = lds_v4i(hi_addr);
+        return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      constexpr int T = S::SM * S::SN;
+      constexpr int STRIDE = T / S::LPS > 0 ? T / S::LPS : 1;
+      if constexpr (E8M0) {
+        // scale exponents: the biased fp32 exponent of 2^e is its E8M0 code;
+        // lane l scales A row l%16 of the strip and B column l%16.  All A strips
+        // stay in registers; B strips are read one column ahead of their MFMAs.
+        const int eb = (int)(__float_as_uint(sb) >> 23);
+        v8i af[S::SM];
+        int ea[S::SM];
+#pragma unroll
+        for (int i = 0; i < S::SM; ++i) {
+          af[i] = frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
+          ea[i] = (int)(__float_as_uint(lds_f32(offR0 + S::strip_scale_off(i) + u * S::S_BYTES)) >> 23);
+        }
+        v8i bcur = frag(offB0[0] + u * S::B_BYTES, offB0[1] + u * S::B_BYTES);
+#pragma unroll
+        for (int j = 0; j < S::SN; ++j) {
+          v8i bnext = bcur;
+          if (j + 1 < S::SN)
+            bnext = frag(offB0[0] + (j + 1) * 2048 + u * S::B_BYTES, offB0[1] + (j + 1) * 2048 + u * S::B_BYTES);
+#pragma unroll
+          for (int i = 0; i < S::SM; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, acc[i][j], 0, 0, 0, ea[i],
+                                                                         0, eb);
+            const int t = j * S::SM + i;
+            if (t % STRIDE == 0 && t / STRIDE < S::LPS) issue_one(t / STRIDE, next, next_u);
+          }
+          bcur = bnext;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
+      v8i bf[S::SN], af[S::SM];
+      v4f sc[S::SM];
+#pragma unroll
+      for (int j = 0; j < S::SN; ++j)
+        bf[j] = frag(offB0[0] + j * 2048 + u * S::B_BYTES, offB0[1] + j * 2048 + u * S::B_BYTES);
+      // A strips are read one strip ahead of their MFMAs, which bounds the live
+      // A fragments to two
+      auto load_strip = [&](int i) {
+        af[i] = frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
+        sc[i] = lds_v4f(offS0 + S::strip_scale_off(i) + u * S::S_BYTES) * sb;
+      };
+      load_strip(0);
+      constexpr int P = 3;
+      v4f part[P];
+#pragma unroll
+      for (int t = 0; t < T + P - 1; ++t) {
+        if (t < T) {
+          if (t % S::SN == 0 && t / S::SN + 1 < S::SM) {
+            // keep the scheduler from hoisting every strip's reads to the top
+            if constexpr (S::SM * S::SN >= 32) __builtin_amdgcn_sched_barrier(0);
+            load_strip(t / S::SN + 1);
+          }
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
+                                                                         0, 0, 0, 0, 0, 0);
+          // spread the LPS loads of the next block over the first MFMAs
+          if (t % STRIDE == 0 && t / STRIDE < S::LPS) issue_one(t / STRIDE, next, next_u);
+        }
+        const int v = t - (P - 1);
+        if (v >= 0) {
+          v4f& a = acc[v / S::SN][v % S::SN];
+          const v4f& q = part[v % P];
+          const v4f& c = sc[v / S::SN];
+          a.x = __builtin_fmaf(q.x, c.x, a.x);
+          a.y = __builtin_fmaf(q.y, c.y, a.y);
+          a.z = __builtin_fmaf(q.z, c.z, a.z);
+          a.w = __builtin_fmaf(q.w, c.w, a.w);
+        }
+      }
+    };
+
+    // ---- K loop over the slot ring, unrolled by NSLOT so slots are constants --
+    // Every step issues the loads of block i+NSLOT-1, clamped to the last
+    // block: past the end the copy lands in the slot just consumed, which no
+    // later block of this item reads.  The schedule is then the same at every
+    // step (NSLOT-2 blocks in flight behind the one awaited) with no branch
+    // between the MFMAs, which would keep the accumulators from being updated
+    // in place.
+    if (kbs > 0) {
+#pragma unroll
+      for (int u = 0; u < NSLOT - 1; ++u) issue(min(u, kbs - 1), u);
+    }
+    for (int i0 = 0; i0 < kbs; i0 += NSLOT) {
+      static_for<NSLOT>([&](auto u_const) {
+        constexpr int u = decltype(u_const)::value;
+        const int i = i0 + u;
+        if (i < kbs) {
+          wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
+          bare_barrier();
+          compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT);
+        }
+      });
+    }
+
+    // ---- epilogue: + C, round to bf16, store the rows that belong to the result
+    // One element at a time in accumulator order (i, j, e): each accumulator
+    // tuple is consumed whole, which keeps register pressure low enough that
+    // the accumulators are never split or spilled around the K loop.
+#pragma unroll
+    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::SN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
+          const int col = n0 + wcol0 + j * 16 + r16;
+          float v = acc[i][j][e];
+          if (C) v += bf16_to_f32(C[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
+          if (row < rows_lim && col < p.N &&
+              (MODE != kContiguous || p.layout[min(row, p.rows - 1)] == group))
+            D[(size_t)row * p.N + col] = f32_to_bf16(v);
+        }
+    // the next item reuses the LDS ring; nothing of this item stays in flight
+    // (without this the compiler assumes a load of this item may still be
+    // pending in the next item's K loop and waits for every load there)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+}  // namespace dg

@@ -173,7 +173,9 @@ def test_decode_split_k_no_stale_partials(dg):
             assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
 
 
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6"])
+# "7" and "8" are the power-of-two-scale kernels, run behind the scale check beside
+# configuration 4: exact inputs take it, the non-power-of-two case must not.
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -182,6 +184,59 @@ def test_dense_every_tile_config(dg, monkeypatch, cfg):
     assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
     q = inputgen.make_dense(200, 300, 1024, seed=15, b_std=0.02, c_std=0.1, pow2=False)
     check_tolerance(run_dense(dg, q), oracle.gemm_nt(q.a, q.sfa, q.b, q.sfb, q.c), f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("pow2", [True, False])
+def test_dense_scale_gate_default_choice(dg, monkeypatch, pow2):
+    # above the size where the library enqueues the scale check and both kernels
+    log(f"case: gated pair 1024x1024x2048 pow2={pow2}")
+    monkeypatch.delenv("DG_FORCE_CONFIG", raising=False)
+    p = inputgen.make_dense(1024, 1040, 2048, seed=21, b_std=0.02, c_std=0.1, pow2=pow2)
+    got = run_dense(dg, p)
+    check_tolerance(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"gate pow2={pow2}")
+
+
+def test_dense_scale_gate_one_bad_scale(dg, monkeypatch):
+    # power-of-two scales except one A scale and, separately, one B scale that
+    # are not: the general kernel must do the work both times
+    log("case: gated pair, a single non-power-of-two scale")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "7")
+    p = inputgen.exact_dense(300, 520, 768, seed=22)
+    for which in ("sfa", "sfb"):
+        s = getattr(p, which).copy()
+        flat = s.reshape(-1)
+        flat[flat.size // 2] *= np.float32(1.5)       # exact: small-integer codes times 3/2
+        args = dict(a=p.a, sfa=p.sfa, b=p.b, sfb=p.sfb)
+        args[which] = s
+        d = sentinel_like((p.M, p.N))
+        dg.dg_fp8_gemm_nt(dev(args["a"]), dev(args["sfa"]), dev(args["b"]), dev(args["sfb"]),
+                          bf16_bits_dev(p.c), d)
+        torch.cuda.synchronize()
+        ref = oracle.gemm_nt(args["a"], args["sfa"], args["b"], args["sfb"], p.c)
+        assert np.array_equal(bits_host(d), ref), which
+
+
+def test_dense_scale_gate_after_other_verdicts(dg, monkeypatch):
+    # alternate pow2 and non-pow2 calls on one stream: each call's verdicts
+    # must be its own
+    log("case: gated pair, alternating scale kinds")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "7")
+    good = inputgen.exact_dense(256, 384, 512, seed=23)
+    bad = inputgen.make_dense(256, 384, 512, seed=24, b_std=0.02, c_std=0.1, pow2=False)
+    outs = []
+    for rep in range(3):
+        for p in (good, bad):
+            d = sentinel_like((p.M, p.N))
+            dg.dg_fp8_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c), d)
+            outs.append((p, d))
+    torch.cuda.synchronize()
+    ref_good = oracle.gemm_nt(good.a, good.sfa, good.b, good.sfb, good.c)
+    ref_bad = oracle.gemm_nt(bad.a, bad.sfa, bad.b, bad.sfb, bad.c)
+    for p, d in outs:
+        if p is good:
+            assert np.array_equal(bits_host(d), ref_good)
+        else:
+            check_tolerance(bits_host(d), ref_bad, "alternating non-pow2")
 
 
 @pytest.mark.slow
@@ -225,7 +280,7 @@ def test_contiguous_small_random(dg):
     check_tolerance(got, ref, "contiguous small")
 
 
-@pytest.mark.parametrize("cfg", ["0", "2", "3", "4", "5", "6"])
+@pytest.mark.parametrize("cfg", ["0", "2", "3", "4", "5", "6", "7", "8"])
 def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: contiguous exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -251,7 +306,7 @@ def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.all(got[~written] == SENTINEL)
 
 
-@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6"])
+@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6", "7", "8"])
 def test_masked_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: masked exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
