@@ -135,7 +135,8 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   // DG_FORCE_CONFIG picks a configuration (a power-of-two one runs gated beside
   // the default general one); DG_SCALE_PATH=1 turns the gated pair off.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
-  if (forced >= 0 && forced < dg::kNumConfigs && (forced != dg::kCfgDecode || mode == dg::kDense) &&
+  if (forced >= 0 && forced < dg::kNumConfigs &&
+      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense) &&
       (mode != dg::kContiguous || dg::config_info(forced).bm <= 128)) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256) {
       ch.cfg = dg::kCfg128x128x2;
@@ -145,7 +146,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
       ch.gated_cfg = -1;
     }
   }
-  if (env_int("DG_SCALE_PATH", 0) == 1 || ch.cfg == dg::kCfgDecode) ch.gated_cfg = -1;
+  if (env_int("DG_SCALE_PATH", 0) == 1 || ch.cfg == dg::kCfgDecode || ch.cfg == dg::kCfgNarrow) ch.gated_cfg = -1;
   if (ch.cfg == dg::kCfgDecode) {
     const int fs = env_int("DG_FORCE_SPLITS", 0);
     if (fs > 0) ch.splits = fs;

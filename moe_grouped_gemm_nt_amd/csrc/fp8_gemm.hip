@@ -260,6 +260,146 @@ splitk_reduce_kernel(Params p) {
   }
 }
 
+// ============================================================================
+// narrow kernel (dense shapes with few rows): the whole K per workgroup
+// ============================================================================
+// A workgroup owns a 16-row x 48-column tile and the whole K, so no partial
+// sums leave it and one launch does all the work.  Its four waves take the K
+// blocks in turn (wave w: blocks w, w+4, ...); each wave streams its blocks
+// through a private ring of NR LDS slots with direct global->LDS loads (8 rows
+// of 128 bytes per instruction: A 16 rows, B 48 rows, the 16 row scales and
+// the B scales of the three 16-column strips) and waits only for its own
+// loads, so the K loop has no barrier.  At the end the four wave totals are
+// summed through LDS in wave order, C is added and the result rounded.  The
+// m-strips of one column slice get workgroup ids of one residue mod 8, so
+// they run on one XCD and read B from one L2.
+constexpr int NWM = 16, NWN = 48;                // tile
+constexpr int NR = 4;                            // slots per wave
+constexpr int NA = NWM * KBLK, NBB = NWN * KBLK; // A / B bytes per block
+constexpr int NSLOTB = NA + NBB + NWM * 4 + 16;  // + row scales + strip B scales
+constexpr int NLPB = NWM / 8 + NWN / 8 + 2;      // loads per block
+static_assert(NLPB * NR < 64, "outstanding loads must fit the 6-bit vmcnt");
+
+__global__ void __launch_bounds__(256)
+fp8_gemm_nt_narrow_kernel(Params p) {
+  constexpr int SN = NWN / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * NR * NSLOTB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int strips = (p.rows + NWM - 1) / NWM;
+  const int slices = (p.N + NWN - 1) / NWN;
+  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int slice = (k / strips) * 8 + xcd, strip = k % strips;
+  if (slice >= slices) return;
+  const int m0 = strip * NWM, n0 = slice * NWN;
+  const int KB = p.K / KBLK;
+  const int NB = (p.N + 127) / 128;
+  const uint32_t ring = lds_u32(smem) + (uint32_t)(wave * NR * NSLOTB);
+
+  // load sources: lane l of a load instruction takes row 8q + l/8, 16-byte
+  // chunk l%8 (stored at its swizzled position)
+  const int lr = lane >> 3;
+  const uint8_t* a_src[NWM / 8];
+  const uint8_t* b_src[NWN / 8];
+#pragma unroll
+  for (int q = 0; q < NWM / 8; ++q) {
+    const int r = q * 8 + lr;
+    a_src[q] = p.a + (size_t)min(m0 + r, p.rows - 1) * p.K + (((lane & 7) ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < NWN / 8; ++q) {
+    const int r = q * 8 + lr;
+    b_src[q] = p.b + (size_t)min(n0 + r, p.N - 1) * p.K + (((lane & 7) ^ swz(r)) << 4);
+  }
+  const float* sa_src = p.sfa + min(m0 + (lane & 15), p.rows - 1);
+  const int strip_nb = min(min(n0 + 16 * min(lane, SN - 1), p.N - 1) / 128, NB - 1);
+  const float* sb_src = p.sfb + (size_t)strip_nb * KB;
+
+  const int nblk = wave < KB ? (KB - wave + 3) / 4 : 0;
+  auto issue = [&](int j, int u) {
+    const int kb = wave + 4 * j;
+    const size_t kofs = (size_t)kb * KBLK;
+    const uint32_t slot = ring + (uint32_t)(u * NSLOTB);
+#pragma unroll
+    for (int q = 0; q < NWM / 8; ++q) dma_16(a_src[q] + kofs, slot + q * 1024);
+#pragma unroll
+    for (int q = 0; q < NWN / 8; ++q) dma_16(b_src[q] + kofs, slot + NA + q * 1024);
+    if (lane < 16) dma_4(sa_src + (size_t)kb * p.rows, slot + NA + NBB);
+    if (lane < SN) dma_4(sb_src + kb, slot + NA + NBB + NWM * 4);
+  };
+  v4f acc[1][SN];
+#pragma unroll
+  for (int c = 0; c < SN; ++c) acc[0][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NR; ++u)
+    if (u < nblk) issue(u, u);
+  for (int j0 = 0; j0 < nblk; j0 += NR) {
+    static_for<NR>([&](auto u_const) {
+      constexpr int u = decltype(u_const)::value;
+      const int j = j0 + u;
+      if (j < nblk) {
+        wait_stages<NLPB, NR - 1>(min(NR - 1, nblk - 1 - j));
+        const uint8_t* base = smem + (wave * NR + u) * NSLOTB;
+        const float* sa = reinterpret_cast<const float*>(base + NA + NBB);
+        v8i bf[SN];
+#pragma unroll
+        for (int c = 0; c < SN; ++c) bf[c] = lds_fragment(base + NA, c * 16 + r16, g16);
+        const v8i af = lds_fragment(base, r16, g16);
+        const v4f sr = *reinterpret_cast<const v4f*>(sa + g16 * 4);
+        v4f q[SN];
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < SN; ++c)
+          q[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[c], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < SN; ++c) {
+          const v4f f = sr * sa[NWM + c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[0][c][e] = __builtin_fmaf(q[c][e], f[e], acc[0][c][e]);
+        }
+        if (j + NR < nblk) {
+          wait_vm_lgkm0<63>();                    // the slot's LDS reads have completed
+          issue(j + NR, u);
+        }
+      }
+    });
+  }
+  // wave totals, summed in wave order through the (now idle) slot memory
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  v4f* red = reinterpret_cast<v4f*>(smem);
+  if (wave > 0) {
+#pragma unroll
+    for (int c = 0; c < SN; ++c) red[((wave - 1) * SN + c) * 64 + lane] = acc[0][c];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int c = 0; c < SN; ++c) acc[0][c] += red[(w * SN + c) * 64 + lane];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = m0 + 4 * g16 + e;
+#pragma unroll
+    for (int c = 0; c < SN; ++c) {
+      const int col = n0 + 16 * c + r16;
+      float v = acc[0][c][e];
+      if (p.c) v += bf16_to_f32(p.c[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
+      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(v);
+    }
+  }
+}
+
+hipError_t launch_narrow(const Params& p, hipStream_t stream) {
+  const int strips = (p.rows + NWM - 1) / NWM;
+  const int slices = (p.N + NWN - 1) / NWN;
+  const int grid = 8 * strips * ((slices + 7) / 8);
+  hipLaunchKernelGGL(fp8_gemm_nt_narrow_kernel, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU = 1>
 hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
   constexpr int threads = WAVES_M * WAVES_N * 64;
@@ -302,6 +442,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     {128, 256, 512, "128x256_w2x4_s3"},
     {128, 256, 256, "e8m0_128x256_w2x2_s3"},
     {128, 256, 512, "e8m0_ws_128x256_w2x2+4_s3"},
+    {NWM, NWN, 256, "narrow_16x48_fullk"},
 };
 
 }  // namespace
@@ -319,6 +460,7 @@ hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t
     case kCfg128x256w8: return launch_cfg<128, 256, 2, 4, 3>(mode, p, grid, stream);
     case kCfgE8_128x256:
     case kCfgWs_128x256: return launch_gemm_e8m0(mode, cfg, p, grid, stream);
+    case kCfgNarrow: return mode == kDense ? launch_narrow(p, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -175,7 +175,7 @@ def test_decode_split_k_no_stale_partials(dg):
 
 # "7" and "8" are the power-of-two-scale kernels, run behind the scale check beside
 # configuration 4: exact inputs take it, the non-power-of-two case must not.
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -184,6 +184,25 @@ def test_dense_every_tile_config(dg, monkeypatch, cfg):
     assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
     q = inputgen.make_dense(200, 300, 1024, seed=15, b_std=0.02, c_std=0.1, pow2=False)
     check_tolerance(run_dense(dg, q), oracle.gemm_nt(q.a, q.sfa, q.b, q.sfb, q.c), f"cfg{cfg}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (1, 8, 128), (17, 200, 640), (100, 520, 1024),
+                                   (64, 2112, 128), (33, 4096, 512), (16, 48, 384), (64, 130, 896)])
+def test_dense_narrow_kernel_exact(dg, monkeypatch, M, N, K):
+    # the whole-K kernel for few rows: exact regime, ragged M, N and block counts
+    log(f"case: narrow kernel exact {M}x{N}x{K}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "9")
+    p = inputgen.exact_dense(M, N, K, seed=M * 7 + K)
+    got = run_dense(dg, p)
+    ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} mismatches"
+
+
+def test_dense_narrow_kernel_decode_random(dg, monkeypatch):
+    log("case: narrow kernel, dense config 1 (64x2112x7168, C) full oracle")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "9")
+    p = inputgen.make_config(1)
+    check_tolerance(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "narrow config1")
 
 
 @pytest.mark.parametrize("pow2", [True, False])
