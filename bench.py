@@ -9,10 +9,18 @@ read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5]
+       python bench.py --calibrate-copy   (a plain device copy of known size, for
+                                           scaling HBM byte counters)
+
+`roofline.traffic` comes from profiles/hbm_traffic.json (HBM bytes per launch
+of the headline kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
+the same counters on a plain copy); it is null when that file is absent or was
+taken from kernel sources other than the current ones.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -41,6 +49,42 @@ SHAPES = {
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+KERNEL_SOURCES = ["fp8_gemm_core.h", "fp8_gemm.hip", "fp8_gemm_e8m0.hip", "dg_api.hip", "dg_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_grouped_gemm_nt_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured for `workload`, if taken from the current kernels."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("workloads", {}).get(workload)
+
+
+def calibrate_copy(torch, reps=20):
+    """Plain device-to-device copies of COPY_BYTES each: the reference the HBM
+    byte counters are scaled by (one copy reads and writes COPY_BYTES)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration: {reps} copies of {COPY_BYTES} bytes")
 
 
 def algorithmic_bytes(p) -> int:
@@ -180,7 +224,7 @@ def main():
     ap.add_argument("--shapes", default="1,2,3,4,5", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -194,6 +238,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     dg.load()
     dg.dg_init()
     shapes = [int(s) for s in args.shapes.split(",") if s.strip()]
@@ -225,13 +272,12 @@ def main():
             torch.cuda.empty_cache()
 
     w, steps, total_ms, ms, tflops, gbs = head
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get(w.name)
+    t = load_traffic(w.name)
+    traffic = int(t["hbm_bytes_per_launch"]) if t else None
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": int(w.bytes), "avg_launch_us": round(ms * 1e3, 3)}
+                "alg_bytes_per_launch": int(w.bytes), "avg_launch_us": round(ms * 1e3, 3),
+                "kernel": "fp8_gemm_nt_narrow_kernel (one launch per call)"}
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the headline workload")

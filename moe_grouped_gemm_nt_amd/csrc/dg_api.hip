@@ -4,9 +4,10 @@
 // Configuration choice (the pages' host heuristics pick a kernel layout and
 // launch shape per problem; prefill and decode shapes get different kernels,
 // zwt0204 DeepGEMM deep dive, "它的核心思路" point 2):
-//   * dense decode shapes (at most 64 rows) take the 64x64 tile with K split
-//     across workgroups, so that enough workgroups stream B from HBM at once,
-//     followed by a split-K reduction kernel;
+//   * dense shapes with at most 64 rows take the narrow kernel (16x48 tiles
+//     over the whole K, one launch) when its tiles occupy at least half the
+//     CUs, else the 64x64 decode tile with K split across workgroups followed
+//     by a split-K reduction kernel;
 //   * large problems enqueue three kernels: a scale check, the power-of-two
 //     kernel (128x256 tiles, scales applied inside the MFMA, loads issued by
 //     dedicated waves) and the general
@@ -120,7 +121,11 @@ constexpr double kGateMinMacs = 2.0e9;
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const int KB = K / 128;
-  if (mode == dg::kDense && rows <= 64 && KB > 0) {
+  if (mode == dg::kDense && rows <= 64 && KB > 0 && ((rows + 15) / 16) * ((N + 47) / 48) >= num_cus / 2) {
+    // few rows, enough 16x48 tiles to occupy half the chip: whole-K tiles, one
+    // launch, nothing crosses workgroups
+    ch.cfg = dg::kCfgNarrow;
+  } else if (mode == dg::kDense && rows <= 64 && KB > 0) {
     // decode: 64x64 tiles; split K so that the workgroups fill the chip while
     // each split keeps at most 8 K blocks, all of them in flight at once
     ch.cfg = dg::kCfgDecode;

@@ -136,6 +136,7 @@ def test_dense_k_zero_gives_c(dg):
 
 def test_dense_split_k_forced_matches(dg, monkeypatch):
     log("case: forced split-K")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
     p = inputgen.exact_dense(64, 640, 4096, seed=13)
     ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
     for splits in ["1", "2", "3", "8"]:
@@ -148,6 +149,7 @@ def test_dense_split_k_forced_matches(dg, monkeypatch):
 @pytest.mark.parametrize("reduction", ["inline", "kernel"])
 def test_decode_split_k_reductions_exact(dg, monkeypatch, reduction):
     log(f"case: decode split-K, {reduction} reduction")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
     monkeypatch.setenv("DG_SPLITK_INLINE", "1" if reduction == "inline" else "0")
     for M, N, K in [(64, 2112, 7168), (17, 200, 2048), (100, 640, 4096)]:
         p = inputgen.exact_dense(M, N, K, seed=M + K)
@@ -159,8 +161,9 @@ def test_decode_split_k_reductions_exact(dg, monkeypatch, reduction):
     monkeypatch.delenv("DG_FORCE_SPLITS")
 
 
-def test_decode_split_k_no_stale_partials(dg):
+def test_decode_split_k_no_stale_partials(dg, monkeypatch):
     log("case: decode split-K, alternating inputs on one workspace")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
     probs = [inputgen.exact_dense(64, 2112, 7168, seed=s) for s in (40, 41, 42)]
     refs = [oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c) for p in probs]
     devs = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
