@@ -9,8 +9,9 @@
 //     CUs, else the 64x64 decode tile with K split across workgroups followed
 //     by a split-K reduction kernel;
 //   * large problems enqueue three kernels: a scale check, the power-of-two
-//     kernel (128x256 tiles, scales applied inside the MFMA, loads issued by
-//     dedicated waves) and the general
+//     kernel (scales applied inside the MFMA: 256x256 tiles of eight waves,
+//     or for the contiguous form 128x256 tiles with dedicated loader waves)
+//     and the general
 //     kernel (128x128 tiles, two workgroups per CU, fp32 promotion); the check
 //     leaves verdicts on the device and exactly one of the two GEMM kernels
 //     does the work, so no host synchronisation is needed;
@@ -135,7 +136,8 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
     if (fill > splits) splits = fill < KB ? fill : KB;
     ch.splits = splits;
   } else if ((double)rows * N * K * (mode == dg::kMasked ? groups : 1) >= kGateMinMacs) {
-    ch.gated_cfg = dg::kCfgWs_128x256;
+    // contiguous tiles must not straddle the 128-row expert segments
+    ch.gated_cfg = mode == dg::kContiguous ? dg::kCfgWs_128x256 : dg::kCfgE8_256x256;
   }
   // DG_FORCE_CONFIG picks a configuration (a power-of-two one runs gated beside
   // the default general one); DG_SCALE_PATH=1 turns the gated pair off.
@@ -143,7 +145,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   if (forced >= 0 && forced < dg::kNumConfigs &&
       ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense) &&
       (mode != dg::kContiguous || dg::config_info(forced).bm <= 128)) {
-    if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256) {
+    if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
       ch.cfg = dg::kCfg128x128x2;
       ch.gated_cfg = forced;
     } else {

@@ -46,6 +46,7 @@ enum Config : int {
   kCfgE8_128x256 = 7, // power-of-two scales only: 128x256 tile, 4 waves of 64x128, 3-slot ring
   kCfgWs_128x256 = 8, // power-of-two scales only: as 7 plus 4 loader waves (wave-specialised)
   kCfgNarrow = 9,     // dense only: 16x48 tile over the whole K, per-wave LDS rings, no split-K
+  kCfgE8_256x256 = 10, // power-of-two scales only: 256x256 tile, 8 waves of 128x64, 2-slot ring
   kNumConfigs
 };
 

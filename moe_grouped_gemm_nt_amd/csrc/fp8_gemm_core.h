@@ -218,7 +218,12 @@ struct Shape {
   static constexpr int A_BYTES = BM * KBLK;     // one slot of each region
   static constexpr int B_BYTES = BN * KBLK;
   static constexpr int RS = BM / NWAVES;        // row scales loaded per wave
-  static constexpr int SA_PER_WAVE = RS + 4;    // RS row scales, this wave's B scale, pad
+  // with 64 row scales per wave the B scale needs a load of its own
+  static constexpr bool SB_SEP = RS >= 64;
+  // a wave's scale area takes a whole 64-lane load (and a second one for the
+  // B scale when SB_SEP), so every lane of the scale loads writes its own word
+  // and the loads need no lane mask: RS row scales, then the B scale
+  static constexpr int SA_PER_WAVE = SB_SEP ? 128 : 64;
   static constexpr int S_BYTES = NWAVES * SA_PER_WAVE * 4;
   // LDS: [A slot 0..NSLOT-1][B slot 0..NSLOT-1][scales slot 0..NSLOT-1]
   static constexpr int B_REGION = NSLOT * A_BYTES;
@@ -226,8 +231,6 @@ struct Shape {
   static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
   static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
   static constexpr int B_INSTR = BN / 8 / NWAVES;
-  // with 64 row scales per wave the B scale needs a load of its own
-  static constexpr bool SB_SEP = RS >= 64;
   static constexpr int LPS = A_INSTR + B_INSTR + 1 + SB_SEP;   // loads per wave per K block
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves per workgroup");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
@@ -418,8 +421,8 @@ fp8_gemm_nt_kernel(Params p) {
       const int gn = min(n0 + r, p.N - 1);
       b_off[j] = (uint32_t)((gn - n0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
     }
-    // scales: lanes < RS load row scales of rows wave*RS + lane, lane RS (or
-    // lane 0 of a separate load when RS is 64) loads this wave's B scale
+    // scales: lanes < RS load row scales of rows wave*RS + lane, the other lanes
+    // (or a separate load when RS is 64) this wave's B scale
     const float* s_src;
     size_t s_stride;                  // elements per K block
     const float* sb_src = SB + (size_t)nb * KB;
@@ -441,9 +444,10 @@ fp8_gemm_nt_kernel(Params p) {
         dma_16s(b_tile + (size_t)i * KBLK, b_off[j],
                 smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
       } else if (!S::SB_SEP || k == S::A_INSTR + S::B_INSTR) {
-        if (lane <= S::RS)
-          dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + wave * S::SA_PER_WAVE * 4);
-      } else if (lane == 0) {
+        // lanes past RS load the B scale (lane RS's copy is the one read)
+        dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + wave * S::SA_PER_WAVE * 4);
+      } else {
+        // every lane loads the B scale; lane 0's copy is the one read
         dma_4(sb_src + i, smem_base + S::S_REGION + u * S::S_BYTES + (wave * S::SA_PER_WAVE + S::RS) * 4);
       }
     };

@@ -172,9 +172,10 @@ fp8_gemm_nt_ws_kernel(Params p) {
         for (int k = 0; k < S::B_INSTR; ++k)
           dma_16s(b_tile + (size_t)i * KBLK, b_off[k],
                   smem_base + S::B_REGION + u * S::B_BYTES + (cw + S::NWAVES * k) * 1024);
-        if (lane <= S::RS)
-          dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + cw * S::SA_PER_WAVE * 4);
-        if (S::SB_SEP && lane == 0)
+        // every lane writes its own word of the wave's scale area (lanes past RS
+        // load the B scale), so the scale loads need no lane mask
+        dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + cw * S::SA_PER_WAVE * 4);
+        if (S::SB_SEP)
           dma_4(sb_src + i, smem_base + S::S_REGION + u * S::S_BYTES + (cw * S::SA_PER_WAVE + S::RS) * 4);
       };
 #pragma unroll
@@ -283,6 +284,7 @@ hipError_t launch_ws(int mode, const Params& p, int grid, hipStream_t stream) {
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
 hipError_t launch_e8(int mode, const Params& p, int grid, hipStream_t stream) {
   constexpr int threads = WAVES_M * WAVES_N * 64;
+  static_assert(threads == 256 || threads == 512, "four or eight waves");
   switch (mode) {
     case kDense:
       hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense, 1, true>), dim3(grid),
@@ -362,6 +364,7 @@ hipError_t launch_scale_check(const float* sfa, size_t na, const float* sfb, siz
 hipError_t launch_gemm_e8m0(int mode, int cfg, const Params& p, int grid, hipStream_t stream) {
   switch (cfg) {
     case kCfgE8_128x256: return launch_e8<128, 256, 2, 2, 3>(mode, p, grid, stream);
+    case kCfgE8_256x256: return launch_e8<256, 256, 2, 4, 2>(mode, p, grid, stream);
     case kCfgWs_128x256: return launch_ws<128, 256, 2, 2, 3>(mode, p, grid, stream);
     default: return hipErrorInvalidValue;
   }

@@ -176,9 +176,9 @@ def test_decode_split_k_no_stale_partials(dg, monkeypatch):
             assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
 
 
-# "7" and "8" are the power-of-two-scale kernels, run behind the scale check beside
+# "7", "8" and "10" are the power-of-two-scale kernels, run behind the scale check beside
 # configuration 4: exact inputs take it, the non-power-of-two case must not.
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -328,7 +328,7 @@ def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.all(got[~written] == SENTINEL)
 
 
-@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6", "7", "8"])
+@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6", "7", "8", "10"])
 def test_masked_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: masked exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
