@@ -8,14 +8,14 @@
 //     over the whole K, one launch) when its tiles occupy at least half the
 //     CUs, else the 64x64 decode tile with K split across workgroups followed
 //     by a split-K reduction kernel;
-//   * large problems enqueue three kernels: a scale check, the power-of-two
-//     kernel (scales applied inside the MFMA: 256x256 tiles of eight waves,
-//     or for the contiguous form 128x256 tiles with dedicated loader waves)
-//     and the general
-//     kernel (128x128 tiles, two workgroups per CU, fp32 promotion); the check
-//     leaves verdicts on the device and exactly one of the two GEMM kernels
-//     does the work, so no host synchronisation is needed;
-//   * the rest take the general kernel alone.
+//   * otherwise the fp32-promotion tile kernel with the largest tile that
+//     still gives every CU a tile (256x256, 128x256, else 128x128 with two
+//     workgroups per CU);
+//   * the power-of-two kernels (scales applied inside the MFMA) are selected
+//     with DG_FORCE_CONFIG; they run behind a scale check that leaves its
+//     verdicts on the device, beside the general kernel, and exactly one of
+//     the two does the work.  On this hardware these shapes are bound by the
+//     loads, not the promotion, so they are not the default.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -114,10 +114,6 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
-// Problems of at least this many multiply-adds take the gated pair; below it
-// the two extra launches would cost more than the faster kernel saves.
-constexpr double kGateMinMacs = 2.0e9;
-
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
@@ -135,12 +131,19 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
     const int fill = num_cus / (tiles > 0 ? tiles : 1);
     if (fill > splits) splits = fill < KB ? fill : KB;
     ch.splits = splits;
-  } else if ((double)rows * N * K * (mode == dg::kMasked ? groups : 1) >= kGateMinMacs) {
-    // contiguous tiles must not straddle the 128-row expert segments
-    ch.gated_cfg = mode == dg::kContiguous ? dg::kCfgWs_128x256 : dg::kCfgE8_256x256;
+  } else {
+    // the largest tile that still gives every CU a tile: per K block a CU
+    // loads (BM+BN)*128 bytes for BM*BN/256 MFMAs, and the loads bound these
+    // kernels, so bigger tiles run faster once the chip is full.  Contiguous
+    // tiles must not straddle the 128-row expert segments.
+    const long long m_rows = (long long)rows * (mode == dg::kMasked ? groups : 1);
+    const long long tiles256 = ((m_rows + 255) / 256) * ((N + 255) / 256);
+    const long long tiles128x256 = ((m_rows + 127) / 128) * ((N + 255) / 256);
+    if (mode != dg::kContiguous && tiles256 >= num_cus) ch.cfg = dg::kCfg256x256w8;
+    else if (tiles128x256 >= num_cus) ch.cfg = dg::kCfg128x256w8;
   }
-  // DG_FORCE_CONFIG picks a configuration (a power-of-two one runs gated beside
-  // the default general one); DG_SCALE_PATH=1 turns the gated pair off.
+  // DG_FORCE_CONFIG picks a configuration; a power-of-two one runs behind the
+  // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced >= 0 && forced < dg::kNumConfigs &&
       ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense) &&
@@ -153,7 +156,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
       ch.gated_cfg = -1;
     }
   }
-  if (env_int("DG_SCALE_PATH", 0) == 1 || ch.cfg == dg::kCfgDecode || ch.cfg == dg::kCfgNarrow) ch.gated_cfg = -1;
+  if (ch.cfg == dg::kCfgDecode || ch.cfg == dg::kCfgNarrow) ch.gated_cfg = -1;
   if (ch.cfg == dg::kCfgDecode) {
     const int fs = env_int("DG_FORCE_SPLITS", 0);
     if (fs > 0) ch.splits = fs;

@@ -47,6 +47,7 @@ enum Config : int {
   kCfgWs_128x256 = 8, // power-of-two scales only: as 7 plus 4 loader waves (wave-specialised)
   kCfgNarrow = 9,     // dense only: 16x48 tile over the whole K, per-wave LDS rings, no split-K
   kCfgE8_256x256 = 10, // power-of-two scales only: 256x256 tile, 8 waves of 128x64, 2-slot ring
+  kCfg256x256w8 = 11, // 256x256 tile, 8 waves of 128x64, 2-slot ring (fp32 promotion)
   kNumConfigs
 };
 

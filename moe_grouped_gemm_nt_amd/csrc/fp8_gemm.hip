@@ -444,6 +444,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     {128, 256, 512, "e8m0_ws_128x256_w2x2+4_s3"},
     {NWM, NWN, 256, "narrow_16x48_fullk"},
     {256, 256, 512, "e8m0_256x256_w2x4_s2"},
+    {256, 256, 512, "256x256_w2x4_s2"},
 };
 
 }  // namespace
@@ -459,6 +460,7 @@ hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t
     case kCfg128x128x2: return launch_cfg<128, 128, 2, 2, 2, 2>(mode, p, grid, stream);
     case kCfg256x128w8: return launch_cfg<256, 128, 4, 2, 3>(mode, p, grid, stream);
     case kCfg128x256w8: return launch_cfg<128, 256, 2, 4, 3>(mode, p, grid, stream);
+    case kCfg256x256w8: return launch_cfg<256, 256, 2, 4, 2>(mode, p, grid, stream);
     case kCfgE8_128x256:
     case kCfgWs_128x256:
     case kCfgE8_256x256: return launch_gemm_e8m0(mode, cfg, p, grid, stream);

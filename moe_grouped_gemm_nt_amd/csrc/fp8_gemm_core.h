@@ -465,9 +465,9 @@ fp8_gemm_nt_kernel(Params p) {
     // one K block from slot u (compile-time): fragments, promotion factors, MFMAs.
     // The loads of block `next` into slot next_u are spread between the MFMAs so
     // the vector-memory queue drains while the matrix cores run.
-    auto compute = [&](auto u_const, int next, int next_u) {
+    auto compute = [&](auto u_const, int next, int next_u, float live) {
       constexpr int u = decltype(u_const)::value;
-      const float sb = lds_f32(offSB + u * S::S_BYTES);
+      const float sb = lds_f32(offSB + u * S::S_BYTES) * live;
       auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) {
         const v4i lo = lds_v4i(lo_addr), hi = lds_v4i(hi_addr);
         return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -516,7 +516,11 @@ fp8_gemm_nt_kernel(Params p) {
         sc[i] = lds_v4f(offS0 + S::strip_scale_off(i) + u * S::S_BYTES) * sb;
       };
       load_strip(0);
-      constexpr int P = 3;
+#ifdef DG_ISSUE_AT_START
+#pragma unroll
+      for (int k = 0; k < S::LPS; ++k) issue_one(k, next, next_u);
+#endif
+      constexpr int P = 2;
       v4f part[P];
 #pragma unroll
       for (int t = 0; t < T + P - 1; ++t) {
@@ -530,7 +534,9 @@ fp8_gemm_nt_kernel(Params p) {
           part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
                                                                          0, 0, 0, 0, 0, 0);
           // spread the LPS loads of the next block over the first MFMAs
+#ifndef DG_ISSUE_AT_START
           if (t % STRIDE == 0 && t / STRIDE < S::LPS) issue_one(t / STRIDE, next, next_u);
+#endif
         }
         const int v = t - (P - 1);
         if (v >= 0) {
@@ -543,6 +549,8 @@ fp8_gemm_nt_kernel(Params p) {
           a.w = __builtin_fmaf(q.w, c.w, a.w);
         }
       }
+      // nothing of the next block is hoisted into this one (bounds live fragments)
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     // ---- K loop over the slot ring, unrolled by NSLOT so slots are constants --
@@ -556,16 +564,33 @@ fp8_gemm_nt_kernel(Params p) {
 #pragma unroll
       for (int u = 0; u < NSLOT - 1; ++u) issue(min(u, kbs - 1), u);
     }
-    for (int i0 = 0; i0 < kbs; i0 += NSLOT) {
-      static_for<NSLOT>([&](auto u_const) {
-        constexpr int u = decltype(u_const)::value;
-        const int i = i0 + u;
-        if (i < kbs) {
+    if constexpr (E8M0) {
+      for (int i0 = 0; i0 < kbs; i0 += NSLOT) {
+        static_for<NSLOT>([&](auto u_const) {
+          constexpr int u = decltype(u_const)::value;
+          const int i = i0 + u;
+          if (i < kbs) {
+            wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
+            bare_barrier();
+            compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, 1.f);
+          }
+        });
+      }
+    } else {
+      // The fp32-promotion path runs a whole number of ring turns: a step past
+      // the last block recomputes a copy of it (the clamped loads put one in
+      // its slot) and promotes it with a zero factor.  Every step is then the
+      // same straight-line code, which keeps the VGPR accumulators in place.
+      const int steps = (kbs + NSLOT - 1) / NSLOT * NSLOT;
+      for (int i0 = 0; i0 < steps; i0 += NSLOT) {
+        static_for<NSLOT>([&](auto u_const) {
+          constexpr int u = decltype(u_const)::value;
+          const int i = i0 + u;
           wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
           bare_barrier();
-          compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT);
-        }
-      });
+          compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, i < kbs ? 1.f : 0.f);
+        });
+      }
     }
 
     // ---- epilogue: + C, round to bf16, store the rows that belong to the result

@@ -178,7 +178,7 @@ def test_decode_split_k_no_stale_partials(dg, monkeypatch):
 
 # "7", "8" and "10" are the power-of-two-scale kernels, run behind the scale check beside
 # configuration 4: exact inputs take it, the non-power-of-two case must not.
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -208,11 +208,12 @@ def test_dense_narrow_kernel_decode_random(dg, monkeypatch):
     check_tolerance(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "narrow config1")
 
 
+@pytest.mark.parametrize("cfg", ["8", "10"])
 @pytest.mark.parametrize("pow2", [True, False])
-def test_dense_scale_gate_default_choice(dg, monkeypatch, pow2):
-    # above the size where the library enqueues the scale check and both kernels
-    log(f"case: gated pair 1024x1024x2048 pow2={pow2}")
-    monkeypatch.delenv("DG_FORCE_CONFIG", raising=False)
+def test_dense_scale_gate_random(dg, monkeypatch, pow2, cfg):
+    # the scale check picks the power-of-two kernel or the general one
+    log(f"case: gated pair cfg {cfg}, 1024x1040x2048 pow2={pow2}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = inputgen.make_dense(1024, 1040, 2048, seed=21, b_std=0.02, c_std=0.1, pow2=pow2)
     got = run_dense(dg, p)
     check_tolerance(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), f"gate pow2={pow2}")
@@ -328,7 +329,7 @@ def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.all(got[~written] == SENTINEL)
 
 
-@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6", "7", "8", "10"])
+@pytest.mark.parametrize("cfg", ["0", "3", "4", "5", "6", "7", "8", "10", "11"])
 def test_masked_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: masked exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
