@@ -277,7 +277,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": int(w.bytes), "avg_launch_us": round(ms * 1e3, 3),
-                "kernel": "fp8_gemm_nt_narrow_kernel (one launch per call)"}
+                "kernel": "fp8_gemm_nt_decode_kernel + splitk_reduce_kernel (two launches per call, timed together)"}
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the headline workload")

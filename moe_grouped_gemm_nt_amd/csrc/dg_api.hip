@@ -45,13 +45,11 @@ int fail(int status, const char* fmt, ...) {
 
 constexpr int kMaxDevices = 64;
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;    // split-K partial tiles
-constexpr int kMaxCounters = 1 << 16;                    // split-K output tiles per call
 
 struct DeviceState {
   bool ready = false;
   int num_cus = 0;
   float* workspace = nullptr;
-  int32_t* counters = nullptr;
   int32_t* verdicts = nullptr;    // scale check results, dg::kCheckWGs entries
 };
 
@@ -75,13 +73,8 @@ int get_device_state(DeviceState** out) {
       st.num_cus = prop.multiProcessorCount;
       e = hipMalloc(&st.workspace, kWorkspaceBytes);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace): %s", hipGetErrorString(e));
-      e = hipMalloc(&st.counters, sizeof(int32_t) * kMaxCounters);
-      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(counters): %s", hipGetErrorString(e));
       e = hipMalloc(&st.verdicts, sizeof(int32_t) * dg::kCheckWGs);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(verdicts): %s", hipGetErrorString(e));
-      e = hipMemset(st.counters, 0, sizeof(int32_t) * kMaxCounters);
-      if (e == hipSuccess) e = hipDeviceSynchronize();
-      if (e != hipSuccess) return fail(DG_ERR_HIP, "clearing split-K counters: %s", hipGetErrorString(e));
       st.ready = true;
     }
   }
@@ -118,13 +111,15 @@ int env_int(const char* name, int dflt) {
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const int KB = K / 128;
-  if (mode == dg::kDense && rows <= 64 && KB > 0 && ((rows + 15) / 16) * ((N + 47) / 48) >= num_cus / 2) {
-    // few rows, enough 16x48 tiles to occupy half the chip: whole-K tiles, one
-    // launch, nothing crosses workgroups
+  const long long tiles128 = (long long)((rows + 127) / 128) * ((N + 127) / 128);
+  if (mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
+    // one 16-row strip and enough 16x48 tiles to occupy half the chip:
+    // whole-K tiles, one launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
-  } else if (mode == dg::kDense && rows <= 64 && KB > 0) {
-    // decode: 64x64 tiles; split K so that the workgroups fill the chip while
-    // each split keeps at most 8 K blocks, all of them in flight at once
+  } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
+    // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
+    // K so that the workgroups fill the chip while each split keeps at most 8
+    // K blocks, all of them in flight at once
     ch.cfg = dg::kCfgDecode;
     const int tiles = ((rows + 63) / 64) * ((N + 63) / 64);
     int splits = (KB + 7) / 8;
@@ -134,20 +129,23 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   } else {
     // the largest tile that still gives every CU a tile: per K block a CU
     // loads (BM+BN)*128 bytes for BM*BN/256 MFMAs, and the loads bound these
-    // kernels, so bigger tiles run faster once the chip is full.  Contiguous
-    // tiles must not straddle the 128-row expert segments.
+    // kernels, so bigger tiles run faster once the chip is full.  With fewer
+    // tiles than CUs, 128x128 tiles with the deepest ring (one workgroup per
+    // CU, three blocks in flight).  Contiguous calls stay at 128-row tiles: a
+    // 256-row tile that spans two experts' segments runs once per expert, and
+    // on the measured expert mixes that costs more than the larger tile saves.
     const long long m_rows = (long long)rows * (mode == dg::kMasked ? groups : 1);
     const long long tiles256 = ((m_rows + 255) / 256) * ((N + 255) / 256);
     const long long tiles128x256 = ((m_rows + 127) / 128) * ((N + 255) / 256);
     if (mode != dg::kContiguous && tiles256 >= num_cus) ch.cfg = dg::kCfg256x256w8;
     else if (tiles128x256 >= num_cus) ch.cfg = dg::kCfg128x256w8;
+    else ch.cfg = dg::kCfg128x128;
   }
   // DG_FORCE_CONFIG picks a configuration; a power-of-two one runs behind the
   // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced >= 0 && forced < dg::kNumConfigs &&
-      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense) &&
-      (mode != dg::kContiguous || dg::config_info(forced).bm <= 128)) {
+      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense)) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
       ch.cfg = dg::kCfg128x128x2;
       ch.gated_cfg = forced;
@@ -205,14 +203,12 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   p.kbs_per_split = ch.kbs;
   p.workspace = st->workspace;
   p.workspace_bytes = kWorkspaceBytes;
-  p.counters = st->counters;
-  p.splitk_inline = env_int("DG_SPLITK_INLINE", 0) ? 1 : 0;
   p.gate_ok = nullptr;
   const int grid = plan(mode, ch.cfg, p, st, ch.gated_cfg >= 0);
   if (grid == 0) return DG_ERR_UNSUPPORTED;
   if (ch.splits > 1) {
     const long long need = (long long)p.tiles_m * p.tiles_n * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
-    if (need > (long long)kWorkspaceBytes || (long long)p.tiles_m * p.tiles_n > kMaxCounters)
+    if (need > (long long)kWorkspaceBytes)
       return fail(DG_ERR_UNSUPPORTED, "split-K workspace of %lld bytes exceeds %zu", need, kWorkspaceBytes);
   }
   hipError_t e = hipSuccess;

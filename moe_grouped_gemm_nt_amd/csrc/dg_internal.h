@@ -21,8 +21,6 @@ struct Params {
   const int32_t* masked_m; // masked: valid rows per group
   float* workspace;        // split-K partial tiles (fp32)
   size_t workspace_bytes;
-  int32_t* counters;       // split-K arrivals per output tile, zero between calls
-  int splitk_inline;       // 1: the last split reduces in the GEMM kernel; 0: separate reduction kernel
   const int32_t* gate_ok;  // scale check verdicts (kernel path gate), or nullptr for no gate
   int rows;                // dense/contiguous: M; masked: max_m
   int N;

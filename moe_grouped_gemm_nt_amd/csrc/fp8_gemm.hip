@@ -15,16 +15,20 @@ namespace {
 // ============================================================================
 constexpr int DBM = 64, DBN = 64;                 // decode tile
 constexpr int DKBS = 8;                           // max K blocks per workgroup
+constexpr int DNW = 4;                            // waves per workgroup
 constexpr int DSLOT = DBM * KBLK + DBN * KBLK + DBM * 4;
 constexpr int DLPB = DBM / 8 + DBN / 8 + 1;       // loads per K block (one wave)
-constexpr int DNPW = DKBS / 4;                    // K blocks per wave
+constexpr int DNPW = DKBS / DNW;                  // K blocks per wave
+constexpr int DT = (DBM / 16) * (DBN / 16);       // 16x16 sub-tiles of the tile
+constexpr int DTPW = DT / DNW;                    // sub-tiles each wave finishes
 static_assert(DBM == 64, "one 64-lane load carries the tile's row scales");
+static_assert(DKBS % DNW == 0 && DT % DNW == 0, "blocks and sub-tiles divide among the waves");
 static_assert(DLPB * DNPW < 64, "outstanding loads must fit the 6-bit vmcnt");
-static_assert(4 * DBM * DBN * 4 <= DKBS * DSLOT, "the wave reduction reuses the slot memory");
+static_assert(DNW * DT * 64 * 16 <= DKBS * DSLOT, "the wave reduction reuses the slot memory");
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * DNW)
 fp8_gemm_nt_decode_kernel(Params p) {
-  constexpr int SM = DBM / 16, SN = DBN / 16, T = SM * SN;
+  constexpr int SM = DBM / 16, SN = DBN / 16, T = DT;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * DSLOT];
 
   const int tid = threadIdx.x;
@@ -49,19 +53,19 @@ fp8_gemm_nt_decode_kernel(Params p) {
   int nb = n0 / 128;
   nb = nb < NB ? nb : NB - 1;
 
-  // this wave's K blocks: kb0 + wave, kb0 + wave + 4, ...
-  const int nown = kbs > wave ? (kbs - wave + 3) / 4 : 0;
+  // this wave's K blocks: kb0 + wave, kb0 + wave + DNW, ...
+  const int nown = kbs > wave ? (kbs - wave + DNW - 1) / DNW : 0;
   float sb[DNPW];
 #pragma unroll
-  for (int j = 0; j < DNPW; ++j) sb[j] = p.sfb[(size_t)nb * KB + min(kb0 + wave + 4 * j, KB - 1)];
+  for (int j = 0; j < DNPW; ++j) sb[j] = p.sfb[(size_t)nb * KB + min(kb0 + wave + DNW * j, KB - 1)];
 
   // issue every load of this wave's blocks: A (64 rows), B (64 rows), A scales
   const int lr = lane >> 3;
 #pragma unroll
   for (int j = 0; j < DNPW; ++j) {
     if (j < nown) {
-      const int kb = kb0 + wave + 4 * j;
-      const uint32_t slot = smem_base + (uint32_t)((wave + 4 * j) * DSLOT);
+      const int kb = kb0 + wave + DNW * j;
+      const uint32_t slot = smem_base + (uint32_t)((wave + DNW * j) * DSLOT);
 #pragma unroll
       for (int q = 0; q < DBM / 8; ++q) {
         const int r = q * 8 + lr;
@@ -89,7 +93,7 @@ fp8_gemm_nt_decode_kernel(Params p) {
   for (int j = 0; j < DNPW; ++j) {
     if (j < nown) {
       wait_stages<DLPB, DNPW - 1>(nown - 1 - j);
-      const uint8_t* base = smem + (wave + 4 * j) * DSLOT;
+      const uint8_t* base = smem + (wave + DNW * j) * DSLOT;
       const float* sa = reinterpret_cast<const float*>(base + (DBM + DBN) * KBLK);
       v4f sc[SM];
 #pragma unroll
@@ -98,166 +102,86 @@ fp8_gemm_nt_decode_kernel(Params p) {
     }
   }
 
-  // ---- sum the four wave totals in wave order; wave w finishes strip w ----
+  // ---- sum the wave totals in wave order; wave w finishes sub-tiles
+  // DTPW*w .. DTPW*w + DTPW-1 (sub-tile t: rows 16*(t/SN), columns 16*(t%SN))
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v4f* red = reinterpret_cast<v4f*>(smem);
 #pragma unroll
   for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t / SN][t % SN];
   __syncthreads();
-  v4f out[SN];
+  v4f out[DTPW];
+  int orow[DTPW], ocol[DTPW];                     // this lane's first row and its column
 #pragma unroll
-  for (int j = 0; j < SN; ++j) {
-    const int t = wave * SN + j;
+  for (int j = 0; j < DTPW; ++j) {
+    const int t = wave * DTPW + j;
     out[j] = red[t * 64 + lane];
 #pragma unroll
-    for (int src = 1; src < 4; ++src) out[j] += red[(src * T + t) * 64 + lane];
+    for (int src = 1; src < DNW; ++src) out[j] += red[(src * T + t) * 64 + lane];
+    orow[j] = m0 + (t / SN) * 16 + g16 * 4;
+    ocol[j] = n0 + (t % SN) * 16 + r16;
   }
 
   if (p.splits > 1) {
-    // fp32 partial, in the result layout: [tile][split][sub-tile][lane]
-    if (!p.splitk_inline) {
-      v4f* ws = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (T * 64);
+    // fp32 partial, in the result layout [tile][split][sub-tile][lane];
+    // splitk_reduce_kernel, launched next on the same stream, sums the splits
+    v4f* ws = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (T * 64);
 #pragma unroll
-      for (int j = 0; j < SN; ++j) ws[(wave * SN + j) * 64 + lane] = out[j];
-      return;
-    }
-    // In-kernel reduction by the last split to arrive.  Partials are written
-    // and read with device-scope (sc1) accesses, which are coherent across the
-    // XCDs' L2 caches without flushing or invalidating them; a split's stores
-    // are complete (vmcnt 0) before its arrival is counted, and the last split
-    // reads them only after it has seen every arrival.
-    // C of this wave's strip, fetched now so its latency hides behind the exchange
-    float cpre[4][SN];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        const int row = min(m0 + wave * 16 + g16 * 4 + e, p.rows - 1), col = min(n0 + j * 16 + r16, p.N - 1);
-        cpre[e][j] = p.c ? bf16_to_f32(p.c[(size_t)row * p.N + col]) : 0.f;
-      }
-    const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
-        p.workspace, 0, (int)(p.workspace_bytes > 0x7fffffff ? 0x7fffffff : p.workspace_bytes), 0x00020000);
-    constexpr int SC1 = 0x10;     // cache-policy bits of a device-scope access
-    const size_t part_base = ((size_t)tile * p.splits) * (T * 64);
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-      __builtin_amdgcn_raw_buffer_store_b128(
-          out[j], ws, (int)(((part_base + (size_t)split * (T * 64)) + (wave * SN + j) * 64 + lane) * 16), 0, SC1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int s_last;
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               p.splits - 1;
-    __syncthreads();
-    if (!s_last) return;
-    constexpr int MAXS = 8;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) out[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.splits; s0 += MAXS) {
-      v4f part[MAXS][SN];
-#pragma unroll
-      for (int u = 0; u < MAXS; ++u)
-        if (s0 + u < p.splits) {
-#pragma unroll
-          for (int j = 0; j < SN; ++j)
-            part[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                ws, (int)((part_base + (size_t)(s0 + u) * (T * 64) + (wave * SN + j) * 64 + lane) * 16), 0, SC1);
-        }
-#pragma unroll
-      for (int u = 0; u < MAXS; ++u)
-        if (s0 + u < p.splits) {
-#pragma unroll
-          for (int j = 0; j < SN; ++j) out[j] += part[u][j];
-        }
-    }
-    if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = m0 + wave * 16 + g16 * 4 + e;
-#pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        const int col = n0 + j * 16 + r16;
-        if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(out[j][e] + cpre[e][j]);
-      }
-    }
+    for (int j = 0; j < DTPW; ++j) __builtin_nontemporal_store(out[j], &ws[(wave * DTPW + j) * 64 + lane]);
     return;
   }
   // single split: + C, round, store
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = m0 + wave * 16 + g16 * 4 + e;
+  for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int col = n0 + j * 16 + r16;
+    for (int j = 0; j < DTPW; ++j) {
+      const int row = orow[j] + e, col = ocol[j];
       if (p.c) out[j][e] += bf16_to_f32(p.c[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
     }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = m0 + wave * 16 + g16 * 4 + e;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int col = n0 + j * 16 + r16;
-      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(out[j][e]);
-    }
-  }
-}
-
-// Split-K reduction of the decode kernel's partials: one 64-lane workgroup per
-// (tile, 16-row strip).  Every load (all splits, C) is issued before any add so
-// one memory round trip covers them; the splits are summed in split order.
-__global__ void __launch_bounds__(64)
-splitk_reduce_kernel(Params p) {
-  constexpr int SN = DBN / 16, T = (DBM / 16) * SN;
-  constexpr int MAXS = 8;                        // splits loaded per pass
-  const int lane = threadIdx.x;
-  const int tile = blockIdx.x / (DBM / 16);
-  const int strip = blockIdx.x % (DBM / 16);
-  int mt, nt;
-  tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int m0 = mt * DBM + strip * 16, n0 = nt * DBN;
-  const v4f* ws = reinterpret_cast<const v4f*>(p.workspace) + (size_t)tile * p.splits * (T * 64);
-
-  float cv[4][SN];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int row = min(m0 + g16 * 4 + e, p.rows - 1), col = min(n0 + j * 16 + r16, p.N - 1);
-      cv[e][j] = p.c ? bf16_to_f32(p.c[(size_t)row * p.N + col]) : 0.f;
+    for (int j = 0; j < DTPW; ++j) {
+      const int row = orow[j] + e, col = ocol[j];
+      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(out[j][e]);
     }
-  v4f acc[SN];
+}
+
+// Split-K reduction of the decode kernel's partials: one 64-lane workgroup per
+// (tile, 16x16 sub-tile), so the small reduction spreads over many CUs.  Each
+// lane issues all its loads (every split's partial, C) before any add, so one
+// memory round trip covers them; the splits are summed in split order.
+__global__ void __launch_bounds__(64)
+splitk_reduce_kernel(Params p) {
+  constexpr int SN = DBN / 16, T = (DBM / 16) * SN;
+  constexpr int MAXS = 16;                       // splits loaded per pass
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x / T;
+  const int t = blockIdx.x % T;                  // sub-tile: strip t / SN, column block t % SN
+  int mt, nt;
+  tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int row0 = mt * DBM + (t / SN) * 16 + g16 * 4;
+  const int col = nt * DBN + (t % SN) * 16 + r16;
+  const v4f* ws = reinterpret_cast<const v4f*>(p.workspace) + (size_t)tile * p.splits * (T * 64) + t * 64 + lane;
+
+  float cv[4];
 #pragma unroll
-  for (int j = 0; j < SN; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 4; ++e)
+    cv[e] = p.c ? bf16_to_f32(p.c[(size_t)min(row0 + e, p.rows - 1) * p.N + min(col, p.N - 1)]) : 0.f;
+  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += MAXS) {
-    v4f part[MAXS][SN];
-#pragma unroll
-    for (int u = 0; u < MAXS; ++u) {
-      if (s0 + u < p.splits) {
-        const v4f* src = ws + (size_t)(s0 + u) * (T * 64);
-#pragma unroll
-        for (int j = 0; j < SN; ++j) part[u][j] = __builtin_nontemporal_load(&src[(strip * SN + j) * 64 + lane]);
-      }
-    }
+    v4f part[MAXS];
 #pragma unroll
     for (int u = 0; u < MAXS; ++u)
-      if (s0 + u < p.splits) {
+      if (s0 + u < p.splits) part[u] = __builtin_nontemporal_load(ws + (size_t)(s0 + u) * (T * 64));
 #pragma unroll
-        for (int j = 0; j < SN; ++j) acc[j] += part[u][j];
-      }
+    for (int u = 0; u < MAXS; ++u)
+      if (s0 + u < p.splits) acc += part[u];
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = m0 + g16 * 4 + e;
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int col = n0 + j * 16 + r16;
-      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(acc[j][e] + cv[e][j]);
-    }
-  }
+  for (int e = 0; e < 4; ++e)
+    if (row0 + e < p.rows && col < p.N) p.d[(size_t)(row0 + e) * p.N + col] = f32_to_bf16(acc[e] + cv[e]);
 }
 
 // ============================================================================
@@ -425,16 +349,17 @@ hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
 hipError_t launch_decode(const Params& p, hipStream_t stream) {
   const int items = p.tiles_m * p.tiles_n * p.splits;
   const int grid = ((items + 7) / 8) * 8;
-  hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel, dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel, dim3(grid), dim3(64 * DNW), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1 || p.splitk_inline) return e;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(p.tiles_m * p.tiles_n * (DBM / 16)), dim3(64), 0, stream, p);
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(p.tiles_m * p.tiles_n * (DBM / 16) * (DBN / 16)), dim3(64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 const ConfigInfo kConfigs[kNumConfigs] = {
     {128, 128, 256, "128x128_w2x2_s4"},
-    {DBM, DBN, 256, "decode_64x64_ksplit"},
+    {DBM, DBN, 64 * DNW, "decode_64x64_ksplit"},
     {128, 64, 256, "128x64_w2x2_s4"},
     {64, 128, 256, "64x128_w1x4_s4"},
     {128, 128, 256, "128x128_w2x2_s2_2wg"},

@@ -282,7 +282,10 @@ fp8_gemm_nt_kernel(Params p) {
   }
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
   __shared__ int s_prefix[MODE == kMasked ? MAX_GROUPS_LDS + 1 : 1];
-  __shared__ int s_flag;
+  // contiguous form: 128-row blocks per tile (segments are 128-row aligned)
+  constexpr int CBLK = BM >= 256 ? BM / 128 : 1;
+  static_assert(CBLK <= 2, "at most two expert blocks per tile");
+  __shared__ int s_group[CBLK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -342,7 +345,12 @@ fp8_gemm_nt_kernel(Params p) {
   const int w_end = min(total, w_begin + per_xcd);
   int g_cur = 0;                                   // masked walker state
 
-  for (int w = w_begin + slot_id; w < w_end; w += slots) {
+  // A contiguous tile whose two 128-row blocks belong to two experts is
+  // visited twice, once per expert (pass 0, 1); each visit stores only the
+  // rows of its own expert.  The second visit is a repeat of the same item
+  // rather than an inner loop, so the K loop keeps a single copy.
+  int pass = 0;
+  for (int w = w_begin + slot_id; w < w_end;) {
     // ---- resolve the work item ---------------------------------------------
     int group = 0, mt, nt, rows_lim = p.rows;
     if constexpr (MODE == kMasked) {
@@ -358,23 +366,34 @@ fp8_gemm_nt_kernel(Params p) {
     } else {
       tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
       if constexpr (MODE == kContiguous) {
-        // the expert of this block of rows: the largest id among its rows
-        // (padding rows may carry -1); all valid ids in a block agree
-        if (wave == 0) {
+        // the expert of each 128-row block of the tile: the largest id among
+        // its rows (padding rows may carry -1); all valid ids in a block agree
+        if (wave < CBLK) {
           int best = -1;
-          for (int r = lane; r < BM; r += 64) {
-            const int row = mt * BM + r;
+          for (int r = lane; r < BM / CBLK; r += 64) {
+            const int row = mt * BM + wave * (BM / CBLK) + r;
             if (row < p.rows) best = max(best, p.layout[row]);
           }
           for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
-          if (lane == 0) s_flag = best;
+          if (lane == 0) s_group[wave] = best;
         }
         __syncthreads();
-        group = s_flag;
+        const int g0 = s_group[0], g1 = s_group[CBLK - 1];
         __syncthreads();
-        if (group < 0 || group >= p.G) continue;   // uniform across the workgroup
+        const bool v0 = g0 >= 0 && g0 < p.G, v1 = g1 >= 0 && g1 < p.G;
+        group = pass == 0 && v0 ? g0 : g1;
+        if (pass == 0 && v0 && v1 && g0 != g1) {
+          pass = 1;                        // visit this tile again for g1
+        } else {
+          pass = 0;
+          w += slots;
+        }
+        if (!v0 && !v1) continue;          // uniform across the workgroup
+      } else {
+        w += slots;
       }
     }
+    if constexpr (MODE == kMasked) w += slots;
 
     const int m0 = mt * BM;
     const int n0 = nt * BN;

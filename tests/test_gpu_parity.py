@@ -146,11 +146,9 @@ def test_dense_split_k_forced_matches(dg, monkeypatch):
     monkeypatch.delenv("DG_FORCE_SPLITS")
 
 
-@pytest.mark.parametrize("reduction", ["inline", "kernel"])
-def test_decode_split_k_reductions_exact(dg, monkeypatch, reduction):
-    log(f"case: decode split-K, {reduction} reduction")
+def test_decode_split_k_exact(dg, monkeypatch):
+    log("case: decode split-K, several split counts")
     monkeypatch.setenv("DG_FORCE_CONFIG", "1")
-    monkeypatch.setenv("DG_SPLITK_INLINE", "1" if reduction == "inline" else "0")
     for M, N, K in [(64, 2112, 7168), (17, 200, 2048), (100, 640, 4096)]:
         p = inputgen.exact_dense(M, N, K, seed=M + K)
         ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
@@ -174,6 +172,37 @@ def test_decode_split_k_no_stale_partials(dg, monkeypatch):
         torch.cuda.synchronize()
         for i in range(3):
             assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
+
+
+def test_decode_split_k_graph_replays(dg, monkeypatch):
+    # two launches per call (partials, then their reduction) captured in a
+    # graph and replayed several times, with eager calls between the replays
+    log("case: decode split-K under graph replay")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+    probs = [inputgen.exact_dense(64, 2112, 7168, seed=s) for s in (50, 51)]
+    refs = [oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c) for p in probs]
+    devs = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
+    outs = [sentinel_like((64, 2112)) for _ in probs]
+    eager = sentinel_like((64, 2112))
+    for i in range(2):                      # warm-up outside the capture (library set-up)
+        dg.dg_fp8_gemm_nt(*devs[i], outs[i])
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(2):
+            dg.dg_fp8_gemm_nt(*devs[i], outs[i])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.view(torch.int16).fill_(SENTINEL - 0x10000)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
+        dg.dg_fp8_gemm_nt(*devs[rep % 2], eager)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(eager), refs[rep % 2]), rep
 
 
 # "7", "8" and "10" are the power-of-two-scale kernels, run behind the scale check beside
@@ -303,7 +332,7 @@ def test_contiguous_small_random(dg):
     check_tolerance(got, ref, "contiguous small")
 
 
-@pytest.mark.parametrize("cfg", ["0", "2", "3", "4", "5", "6", "7", "8"])
+@pytest.mark.parametrize("cfg", ["0", "2", "3", "4", "5", "6", "7", "8", "10", "11"])
 def test_contiguous_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: contiguous exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -349,8 +378,12 @@ def test_masked_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.all(got[~written] == SENTINEL)
 
 
-def test_contiguous_exact_with_padding_ids_and_empty_expert(dg):
-    log("case: contiguous exact, -1 padding rows, an empty expert, C")
+@pytest.mark.parametrize("cfg", [None, "5", "11"])
+def test_contiguous_exact_with_padding_ids_and_empty_expert(dg, monkeypatch, cfg):
+    # with 256-row tiles two of the three tiles hold two experts each
+    log(f"case: contiguous exact, -1 padding rows, an empty expert, C, config {cfg}")
+    if cfg is not None:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     G, N, K = 5, 200, 512
     rng = np.random.default_rng(3)
     counts = np.array([130, 0, 7, 256, 1])
