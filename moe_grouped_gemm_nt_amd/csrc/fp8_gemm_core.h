@@ -431,7 +431,9 @@ fp8_gemm_nt_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < S::A_INSTR; ++j) {
       const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
-      const int grow = min(m0 + r, a_rows - 1);       // rows past the end are never stored
+      // rows past the valid ones (the end of A, or of a masked group's rows) are
+      // never stored: they re-read the last valid row, whose lines the L1 holds
+      const int grow = min(m0 + r, rows_lim - 1);
       a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
     }
 #pragma unroll
@@ -446,7 +448,7 @@ fp8_gemm_nt_kernel(Params p) {
     size_t s_stride;                  // elements per K block
     const float* sb_src = SB + (size_t)nb * KB;
     if (lane < S::RS) {
-      const int grow = min(m0 + wave * S::RS + lane, a_rows - 1);
+      const int grow = min(m0 + wave * S::RS + lane, rows_lim - 1);
       s_src = SA + grow;
       s_stride = a_rows;
     } else {

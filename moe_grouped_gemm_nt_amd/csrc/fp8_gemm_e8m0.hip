@@ -143,7 +143,7 @@ fp8_gemm_nt_ws_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < S::A_INSTR; ++j) {
         const int r = (cw + S::NWAVES * j) * 8 + (lane >> 3);
-        const int grow = min(m0 + r, a_rows - 1);
+        const int grow = min(m0 + r, rows_lim - 1);   // rows past the valid ones are never stored
         a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
       }
 #pragma unroll
@@ -158,7 +158,7 @@ fp8_gemm_nt_ws_kernel(Params p) {
       const float* s_src;
       size_t s_stride;
       if (lane < S::RS) {
-        s_src = SA + min(m0 + cw * S::RS + lane, a_rows - 1);
+        s_src = SA + min(m0 + cw * S::RS + lane, rows_lim - 1);
         s_stride = a_rows;
       } else {
         s_src = sb_src;
