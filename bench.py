@@ -3,12 +3,13 @@
 One step is one library call over one batch of synthetic inputs already
 resident in HBM.  The headline workload is the dense decode shape
 M=64 N=2112 K=7168 (A ~ N(0,1), B ~ N(0,0.02), 1x128 / 128x128 power-of-two
-scales, bf16 C ~ N(0,0.1)); the other four workloads are reported per shape
-in the same JSON line.  Inputs rotate over enough copies that successive steps
+scales, bf16 C ~ N(0,0.1)); the other four workloads, and the prefill problem
+with K-major operands (nn, tn, tt), are reported per shape in the same JSON
+line.  Inputs rotate over enough copies that successive steps
 read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5,6,7,8]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
 
@@ -44,7 +45,14 @@ SHAPES = {
     3: ("dense_prefill_4096x7168x16384", "mfma"),
     4: ("contiguous_8x4096x7168_rows8192", "mfma"),
     5: ("masked_32x256x4096x7168", "hbm"),
+    # the prefill problem with K-major operands (A stored [K][M] for "t", B
+    # stored [K][N] for a second "n"): same values, same flops and bytes
+    6: ("dense_prefill_4096x7168x16384_nn", "mfma"),
+    7: ("dense_prefill_4096x7168x16384_tn", "mfma"),
+    8: ("dense_prefill_4096x7168x16384_tt", "mfma"),
 }
+LAYOUT_OF = {6: "nn", 7: "tn", 8: "tt"}
+PROBLEM_OF = {6: 3, 7: 3, 8: 3}        # workload index whose generated problem a layout entry reuses
 
 
 def log(msg):
@@ -116,8 +124,9 @@ class Workload:
     def __init__(self, idx, torch, dg, copies=None):
         import inputgen
         t0 = time.time()
-        self.p = p = inputgen.make_config(idx - 1, seed=0)
+        self.p = p = inputgen.make_config(PROBLEM_OF.get(idx, idx) - 1, seed=0)
         self.name, self.bound = SHAPES[idx]
+        self.layout = LAYOUT_OF.get(idx, "nt")
         self.flops = p.flops
         self.bytes = algorithmic_bytes(p)
         per_copy = p.a.nbytes + p.b.nbytes
@@ -130,7 +139,9 @@ class Workload:
             t = torch.from_numpy(np.ascontiguousarray(x))
             return (t.view(dtype) if dtype is not None else t).to(dev)
 
-        a, sfa, b, sfb = up(p.a), up(p.sfa), up(p.b), up(p.sfb)
+        a_st = p.a if self.layout[0] == "n" else np.ascontiguousarray(p.a.T)
+        b_st = p.b if self.layout[1] == "t" else np.ascontiguousarray(p.b.T)
+        a, sfa, b, sfb = up(a_st), up(p.sfa), up(b_st), up(p.sfb)
         self.sets = []
         for i in range(copies):
             s = dict(a=a if i == 0 else a.clone(), sfa=sfa if i == 0 else sfa.clone(),
@@ -154,7 +165,7 @@ class Workload:
         s = self.sets[i % self.copies]
         dg = self.dg
         if self.kind == "Dense":
-            dg.dg_fp8_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
+            getattr(dg, "dg_fp8_gemm_" + self.layout)(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
         elif self.kind == "Contiguous":
             dg.dg_m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"], s["layout"])
         else:
@@ -221,7 +232,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="1,2,3,4,5", help="comma-separated 1-based workload indices")
+    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")

@@ -66,6 +66,24 @@ typedef enum {
 int dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, const float* sfb,
                    const void* c, void* d, int M, int N, int K, void* stream);
 
+/* Dense FP8 GEMM with K-major operands (likun.im section 一: the family
+ * fp8_gemm_{nt,nn,tn,tt}; the first letter gives A's storage, the second B's,
+ * "n" for A meaning [M][K] and "t" [K][M], "t" for B meaning [N][K] and "n"
+ * [K][N]).  Same arithmetic, scales (sfa [K/128][M], sfb [ceil(N/128)][K/128],
+ * indexed by the logical row, column and K block whatever the storage), C and
+ * D as dg_fp8_gemm_nt:
+ *   nn: a [M][K] (K contiguous), b [K][N] (N contiguous)
+ *   tn: a [K][M] (M contiguous), b [K][N] (N contiguous)
+ *   tt: a [K][M] (M contiguous), b [N][K] (K contiguous)
+ * An operand stored [K][M] needs M % 16 == 0, one stored [K][N] needs
+ * N % 16 == 0; other sizes return DG_ERR_UNSUPPORTED.  Returns a dg_status. */
+int dg_fp8_gemm_nn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const void* c, void* d, int M, int N, int K, void* stream);
+int dg_fp8_gemm_tn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const void* c, void* d, int M, int N, int K, void* stream);
+int dg_fp8_gemm_tt(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const void* c, void* d, int M, int N, int K, void* stream);
+
 /* M-grouped GEMM, contiguous layout (likun.im section 二:
  * "m_grouped_..._gemm_nt_contiguous" taking grouped_layout): the rows of every
  * expert are concatenated along M.  grouped_layout is a device int32 array of

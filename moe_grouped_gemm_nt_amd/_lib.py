@@ -21,6 +21,9 @@ DG_ERR_HIP = -3
 
 EXPORTED = [
     "dg_fp8_gemm_nt",
+    "dg_fp8_gemm_nn",
+    "dg_fp8_gemm_tn",
+    "dg_fp8_gemm_tt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
     "dg_init",
@@ -48,8 +51,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             raise RuntimeError(f"{path} is missing: build it with `python -m moe_grouped_gemm_nt_amd.build`")
         lib = ctypes.CDLL(path)
         vp, fp, i32p, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
-        lib.dg_fp8_gemm_nt.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp]
-        lib.dg_fp8_gemm_nt.restype = ci
+        for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+            getattr(lib, name).argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp]
+            getattr(lib, name).restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, vp]
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
@@ -113,6 +117,34 @@ def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
         _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
         _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
         _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
+
+
+def _dense_layout(fn, a, sfa, b, sfb, c, d, M, N, K, stream):
+    _check(fn, getattr(load(), fn)(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
+
+
+def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """d[M][N] = bf16(c + a[M][K] . b[K][N]) (B stored K-major), scales as in the NT call."""
+    M, K = a.shape
+    N = b.shape[1]
+    _dense_layout("dg_fp8_gemm_nn", a, sfa, b, sfb, c, d, M, N, K, stream)
+
+
+def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """d[M][N] = bf16(c + a[K][M]^T . b[K][N]) (both operands stored K-major)."""
+    K, M = a.shape
+    N = b.shape[1]
+    _dense_layout("dg_fp8_gemm_tn", a, sfa, b, sfb, c, d, M, N, K, stream)
+
+
+def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """d[M][N] = bf16(c + a[K][M]^T . b[N][K]^T) (A stored K-major)."""
+    K, M = a.shape
+    N = b.shape[0]
+    _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, M, N, K, stream)
 
 
 def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:

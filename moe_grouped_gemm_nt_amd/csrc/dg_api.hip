@@ -108,15 +108,17 @@ int env_int(const char* name, int dflt) {
 }
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
-Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
+// kmajor: a dense call with a K-major operand (nn, tn, tt), which only the
+// 128x128, 128x256 and 256x256 tile kernels read
+Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, bool kmajor) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const int KB = K / 128;
   const long long tiles128 = (long long)((rows + 127) / 128) * ((N + 127) / 128);
-  if (mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
+  if (!kmajor && mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
     // one 16-row strip and enough 16x48 tiles to occupy half the chip:
     // whole-K tiles, one launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
-  } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
+  } else if (!kmajor && mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
     // K blocks, all of them in flight at once
@@ -144,7 +146,9 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus) {
   // DG_FORCE_CONFIG picks a configuration; a power-of-two one runs behind the
   // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
-  if (forced >= 0 && forced < dg::kNumConfigs &&
+  const bool forced_ok = !kmajor || forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 ||
+                         forced == dg::kCfg256x256w8;
+  if (forced >= 0 && forced < dg::kNumConfigs && forced_ok &&
       ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense)) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
       ch.cfg = dg::kCfg128x128x2;
@@ -197,7 +201,7 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
-  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus);
+  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout != 0);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
@@ -254,6 +258,48 @@ extern "C" int dg_fp8_gemm_nt(const void* a, const float* sfa, const void* b, co
   p.K = K;
   p.G = 1;
   return launch(dg::kDense, p, M, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+// Dense call with K-major operands: layout bit 0 = A is [K][M], bit 1 = B is [K][N].
+int dense_kmajor(const void* a, const float* sfa, const void* b, const float* sfb, const void* c, void* d,
+                 int M, int N, int K, int layout, void* stream) {
+  int s = check_common(a, sfa, b, sfb, c, d, M, N, K);
+  if (s != DG_OK) return s;
+  if ((layout & 1) && M % 16 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "A stored [K][M] needs M %% 16 == 0 (M=%d)", M);
+  if ((layout & 2) && N % 16 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "B stored [K][N] needs N %% 16 == 0 (N=%d)", N);
+  if (M == 0 || N == 0) return DG_OK;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.G = 1;
+  p.ab_layout = layout;
+  return launch(dg::kDense, p, M, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" int dg_fp8_gemm_nn(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const void* c, void* d, int M, int N, int K, void* stream) {
+  return dense_kmajor(a, sfa, b, sfb, c, d, M, N, K, 2, stream);
+}
+
+extern "C" int dg_fp8_gemm_tn(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const void* c, void* d, int M, int N, int K, void* stream) {
+  return dense_kmajor(a, sfa, b, sfb, c, d, M, N, K, 3, stream);
+}
+
+extern "C" int dg_fp8_gemm_tt(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const void* c, void* d, int M, int N, int K, void* stream) {
+  return dense_kmajor(a, sfa, b, sfb, c, d, M, N, K, 1, stream);
 }
 
 extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,

@@ -30,6 +30,7 @@ struct Params {
   int tiles_n;             // ceil(N / BN)
   int splits;              // split-K factor (>= 1; decode kernel only)
   int kbs_per_split;       // K blocks per split (decode kernel only)
+  int ab_layout;           // dense: bit 0 = A stored [K][M], bit 1 = B stored [K][N] (0 = nt)
 };
 
 // Tile configurations compiled into the library.

@@ -324,9 +324,32 @@ hipError_t launch_narrow(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Dense calls with K-major operands (nn, tn, tt) are compiled for the tiles
+// the chooser gives them: 128x128 (four waves, 4-slot ring), 128x256 and 256x256.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU, int LAYOUT>
+hipError_t launch_dense_layout(const Params& p, int grid, hipStream_t stream) {
+  constexpr bool compiled = WG_PER_CU == 1 && ((BM == 128 && BN == 128 && NSLOT == 4) ||
+                                               (BM == 128 && BN == 256) || (BM == 256 && BN == 256));
+  if constexpr (compiled) {
+    hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense, WG_PER_CU, false, LAYOUT>),
+                       dim3(grid), dim3(WAVES_M * WAVES_N * 64), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU = 1>
 hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
   constexpr int threads = WAVES_M * WAVES_N * 64;
+  if (mode == kDense && p.ab_layout != 0) {
+    switch (p.ab_layout) {
+      case 1: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 1>(p, grid, stream);
+      case 2: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 2>(p, grid, stream);
+      case 3: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 3>(p, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (mode) {
     case kDense:
       hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kDense, WG_PER_CU, false>), dim3(grid),

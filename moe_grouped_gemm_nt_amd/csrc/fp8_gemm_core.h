@@ -60,6 +60,7 @@
 namespace dg {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -204,6 +205,45 @@ __device__ __forceinline__ void static_for_impl(F&& f) {
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
+// ---- K-major ("t" / second-"n") operands ----------------------------------
+// A K block of an operand stored [K][rows] (rows contiguous) is 128 K rows of
+// X bytes (X = the tile's BM or BN).  In LDS it is kept in units of 8 K rows
+// ("octets", X/2 16-byte slots each); inside octet o, 16-byte chunk c of K row
+// r (columns 16c..16c+15) sits at slot 8*(c ^ odd(o)) + r, odd(o) = (o/4) & 1.
+// The 8 rows of one chunk are then 128 contiguous bytes, and the octets that
+// lanes 16..31 (48..63) read hold each chunk in the other 128-byte half of the
+// 256 bytes the LDS banks cover than the octets lanes 0..15 (32..47) read, so
+// a transposing read has no bank conflict.  The direct loads fill slot s of
+// the block (s = 64 * instruction + lane).
+template <int X>
+__device__ __forceinline__ void kmajor_slot(int s, int& krow, int& chunk) {
+  const int octet = s / (X / 2), rem = s % (X / 2);
+  krow = 8 * octet + (rem & 7);
+  chunk = (rem >> 3) ^ ((octet >> 2) & 1);
+}
+// ds_read_b64_tr_b8 (measured lane layout): in each group of 16 lanes, lane i
+// < 8 receives byte i of the 8-byte words addressed by the group's even lanes
+// 0, 2, .., 14 (in that order) and lane 8 + i byte i of the odd lanes' words.
+// A fragment lane (row r = l % 16, K bytes 32*(l/16) .. +31) is gathered by four
+// such reads, t = 0..3, in which lane s of the group addresses K row
+// 32*(l/16) + 8t + s/2 at column row0 + 16*i + 8*(s%2) of 16-row strip i.
+// With row0 a multiple of 32, strip i's address is
+// kmajor_frag_base(row0, lane, i & 1) + 128*i + 8*X*t.
+template <int X>
+__device__ __forceinline__ uint32_t kmajor_frag_base(int row0, int lane, int parity) {
+  const int odd = (lane >> 4) & 1;
+  return (uint32_t)(32 * X * (lane >> 4) + 8 * (row0 + (lane & 15)) + (parity ? -128 : 128) * odd);
+}
+template <int X>
+__device__ __forceinline__ v8i kmajor_frag(uint32_t addr) {
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  const v2i q0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_v2i*>(static_cast<uintptr_t>(addr)));
+  const v2i q1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_v2i*>(static_cast<uintptr_t>(addr + 8 * X)));
+  const v2i q2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_v2i*>(static_cast<uintptr_t>(addr + 16 * X)));
+  const v2i q3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_v2i*>(static_cast<uintptr_t>(addr + 24 * X)));
+  return (v8i){q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+}
+
 // ============================================================================
 // prefill / grouped kernel
 // ============================================================================
@@ -267,10 +307,16 @@ __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32
 // E8M0 = false: MFMA partials promoted by fp32 FMAs (any scales).
 // E8M0 = true:  every scale is a power of two, applied by the MFMA itself from
 //               its E8M0 exponent; results accumulate in place (AGPRs).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU, bool E8M0>
+// LAYOUT: bit 0 set = A is stored K-major ([K][M], M contiguous: the "t" of
+//         "tn"/"tt"), bit 1 set = B is stored [K][N] (the second "n" of
+//         "nn"/"tn"); clear bits are the K-contiguous "nt" operands.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU, bool E8M0, int LAYOUT = 0>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WG_PER_CU)
 fp8_gemm_nt_kernel(Params p) {
   using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT>;
+  constexpr bool TA = (LAYOUT & 1) != 0, TB = (LAYOUT & 2) != 0;
+  static_assert(LAYOUT == 0 || MODE == kDense, "K-major operands are supported by the dense form");
+  static_assert((!TA || S::WTM % 32 == 0) && (!TB || S::WTN % 32 == 0), "K-major strips pair up in 32-row steps");
   // Path gate: the scale check kernel leaves one verdict per check workgroup;
   // the E8M0 kernel runs only if all scales are powers of two, the other
   // kernel only if not.  Every lane reads the same verdicts, so the exit is
@@ -303,11 +349,15 @@ fp8_gemm_nt_kernel(Params p) {
   // per-lane LDS addresses of the fragments of strip 0 in slot 0; strip i and
   // slot u add the constants 2048*i and u*region bytes (the swizzle repeats
   // every 16 rows)
+  // (a K-major operand: the bases of the lane's transposing reads for even and
+  // for odd strips, see kmajor_frag_base)
   uint32_t offA0[2], offB0[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    offA0[h] = smem_base + (wrow0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4);
-    offB0[h] = smem_base + S::B_REGION + (wcol0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4);
+    offA0[h] = smem_base + (TA ? kmajor_frag_base<BM>(wrow0, lane, h)
+                               : (wrow0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4));
+    offB0[h] = smem_base + S::B_REGION + (TB ? kmajor_frag_base<BN>(wcol0, lane, h)
+                                             : (wcol0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4));
   }
   // row scales of the lane's four result rows in strip 0 (strip i adds strip_scale_off(i))
   const uint32_t offS0 = smem_base + S::S_REGION +
@@ -425,22 +475,40 @@ fp8_gemm_nt_kernel(Params p) {
     // at LDS byte 16*l of that 1 KB piece: row 8*(...) + l/8, physical chunk l%8,
     // which holds logical chunk (l%8) ^ swz(row).  Uniform bases (tile origin,
     // K block) live in SGPRs; lanes add a 32-bit offset inside the tile.
-    const uint8_t* a_tile = A + (size_t)m0 * p.K;
-    const uint8_t* b_tile = B + (size_t)n0 * p.K;
+    // A K-major operand's tile starts at column m0 (n0) of its [K][rows] array
+    // and a K block advances 128 of its rows; chunks of columns past the valid
+    // ones re-read the last valid 16 columns (rows_lim and N are multiples of
+    // 16 for such operands), whose results are never stored.
+    const uint8_t* a_tile = TA ? A + m0 : A + (size_t)m0 * p.K;
+    const uint8_t* b_tile = TB ? B + n0 : B + (size_t)n0 * p.K;
+    const size_t a_kstep = TA ? (size_t)KBLK * a_rows : KBLK;
+    const size_t b_kstep = TB ? (size_t)KBLK * p.N : KBLK;
     uint32_t a_off[S::A_INSTR], b_off[S::B_INSTR];
 #pragma unroll
     for (int j = 0; j < S::A_INSTR; ++j) {
-      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
-      // rows past the valid ones (the end of A, or of a masked group's rows) are
-      // never stored: they re-read the last valid row, whose lines the L1 holds
-      const int grow = min(m0 + r, rows_lim - 1);
-      a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+      if constexpr (TA) {
+        int kr, c;
+        kmajor_slot<BM>(64 * (wave + S::NWAVES * j) + lane, kr, c);
+        a_off[j] = (uint32_t)(kr * a_rows + (min(m0 + 16 * c, rows_lim - 16) - m0));
+      } else {
+        const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+        // rows past the valid ones (the end of A, or of a masked group's rows) are
+        // never stored: they re-read the last valid row, whose lines the L1 holds
+        const int grow = min(m0 + r, rows_lim - 1);
+        a_off[j] = (uint32_t)((grow - m0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+      }
     }
 #pragma unroll
     for (int j = 0; j < S::B_INSTR; ++j) {
-      const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
-      const int gn = min(n0 + r, p.N - 1);
-      b_off[j] = (uint32_t)((gn - n0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+      if constexpr (TB) {
+        int kr, c;
+        kmajor_slot<BN>(64 * (wave + S::NWAVES * j) + lane, kr, c);
+        b_off[j] = (uint32_t)(kr * p.N + (min(n0 + 16 * c, p.N - 16) - n0));
+      } else {
+        const int r = (wave + S::NWAVES * j) * 8 + (lane >> 3);
+        const int gn = min(n0 + r, p.N - 1);
+        b_off[j] = (uint32_t)((gn - n0) * p.K) + (((lane & 7) ^ swz(r)) << 4);
+      }
     }
     // scales: lanes < RS load row scales of rows wave*RS + lane, the other lanes
     // (or a separate load when RS is 64) this wave's B scale
@@ -459,10 +527,10 @@ fp8_gemm_nt_kernel(Params p) {
     // the k-th load instruction (k < LPS) of K block i into slot u
     auto issue_one = [&](int k, int i, int u) {
       if (k < S::A_INSTR) {
-        dma_16s(a_tile + (size_t)i * KBLK, a_off[k], smem_base + u * S::A_BYTES + (wave + S::NWAVES * k) * 1024);
+        dma_16s(a_tile + i * a_kstep, a_off[k], smem_base + u * S::A_BYTES + (wave + S::NWAVES * k) * 1024);
       } else if (k < S::A_INSTR + S::B_INSTR) {
         const int j = k - S::A_INSTR;
-        dma_16s(b_tile + (size_t)i * KBLK, b_off[j],
+        dma_16s(b_tile + i * b_kstep, b_off[j],
                 smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
       } else if (!S::SB_SEP || k == S::A_INSTR + S::B_INSTR) {
         // lanes past RS load the B scale (lane RS's copy is the one read)
@@ -493,6 +561,15 @@ fp8_gemm_nt_kernel(Params p) {
         const v4i lo = lds_v4i(lo_addr), hi = lds_v4i(hi_addr);
         return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       };
+      // fragments of 16-row strip i of A / 16-column strip j of B in slot u
+      auto fragA = [&](int i) {
+        if constexpr (TA) return kmajor_frag<BM>(offA0[i & 1] + i * 128 + u * S::A_BYTES);
+        else return frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
+      };
+      auto fragB = [&](int j) {
+        if constexpr (TB) return kmajor_frag<BN>(offB0[j & 1] + j * 128 + u * S::B_BYTES);
+        else return frag(offB0[0] + j * 2048 + u * S::B_BYTES, offB0[1] + j * 2048 + u * S::B_BYTES);
+      };
       constexpr int T = S::SM * S::SN;
       constexpr int STRIDE = T / S::LPS > 0 ? T / S::LPS : 1;
       if constexpr (E8M0) {
@@ -504,15 +581,15 @@ fp8_gemm_nt_kernel(Params p) {
         int ea[S::SM];
 #pragma unroll
         for (int i = 0; i < S::SM; ++i) {
-          af[i] = frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
+          af[i] = fragA(i);
           ea[i] = (int)(__float_as_uint(lds_f32(offR0 + S::strip_scale_off(i) + u * S::S_BYTES)) >> 23);
         }
-        v8i bcur = frag(offB0[0] + u * S::B_BYTES, offB0[1] + u * S::B_BYTES);
+        v8i bcur = fragB(0);
 #pragma unroll
         for (int j = 0; j < S::SN; ++j) {
           v8i bnext = bcur;
           if (j + 1 < S::SN)
-            bnext = frag(offB0[0] + (j + 1) * 2048 + u * S::B_BYTES, offB0[1] + (j + 1) * 2048 + u * S::B_BYTES);
+            bnext = fragB(j + 1);
 #pragma unroll
           for (int i = 0; i < S::SM; ++i) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bcur, acc[i][j], 0, 0, 0, ea[i],
@@ -529,18 +606,14 @@ fp8_gemm_nt_kernel(Params p) {
       v4f sc[S::SM];
 #pragma unroll
       for (int j = 0; j < S::SN; ++j)
-        bf[j] = frag(offB0[0] + j * 2048 + u * S::B_BYTES, offB0[1] + j * 2048 + u * S::B_BYTES);
+        bf[j] = fragB(j);
       // A strips are read one strip ahead of their MFMAs, which bounds the live
       // A fragments to two
       auto load_strip = [&](int i) {
-        af[i] = frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
+        af[i] = fragA(i);
         sc[i] = lds_v4f(offS0 + S::strip_scale_off(i) + u * S::S_BYTES) * sb;
       };
       load_strip(0);
-#ifdef DG_ISSUE_AT_START
-#pragma unroll
-      for (int k = 0; k < S::LPS; ++k) issue_one(k, next, next_u);
-#endif
       constexpr int P = 2;
       v4f part[P];
 #pragma unroll
@@ -555,9 +628,7 @@ fp8_gemm_nt_kernel(Params p) {
           part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
                                                                          0, 0, 0, 0, 0, 0);
           // spread the LPS loads of the next block over the first MFMAs
-#ifndef DG_ISSUE_AT_START
           if (t % STRIDE == 0 && t / STRIDE < S::LPS) issue_one(t / STRIDE, next, next_u);
-#endif
         }
         const int v = t - (P - 1);
         if (v >= 0) {

@@ -14,6 +14,7 @@ from .fp8_gemm import (  # noqa: F401
     round_f64_to_bf16_bits,
     gemm_nt_acc,
     gemm_nt,
+    gemm_layout,
     m_grouped_contiguous,
     m_grouped_masked,
 )

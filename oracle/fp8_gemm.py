@@ -140,6 +140,21 @@ def gemm_nt(a, sfa, b, sfb, c=None, rows=None, cols=None) -> np.ndarray:
     return round_f64_to_bf16_bits(gemm_nt_acc(a, sfa, b, sfb, c, rows, cols))
 
 
+def gemm_layout(layout, a, sfa, b, sfb, c=None, rows=None, cols=None) -> np.ndarray:
+    """bf16 bits of D = C + A.B for the four storage layouts of the dense GEMM
+    family ([likun] section 一: fp8_gemm_{nt,nn,tn,tt}).
+
+    layout is two letters: the first gives A's storage ("n": [M][K], "t":
+    [K][M]), the second B's ("t": [N][K], "n": [K][N]).  Scales are indexed by
+    the logical row, column and K block exactly as in gemm_nt, whatever the
+    storage.  Transposing a stored operand only relabels its values, so the
+    operands are brought to the NT storage and gemm_nt computes."""
+    assert len(layout) == 2 and layout[0] in "nt" and layout[1] in "nt", layout
+    a_nt = np.asarray(a) if layout[0] == "n" else np.ascontiguousarray(np.asarray(a).T)
+    b_nt = np.asarray(b) if layout[1] == "t" else np.ascontiguousarray(np.asarray(b).T)
+    return gemm_nt(a_nt, sfa, b_nt, sfb, c, rows, cols)
+
+
 def m_grouped_contiguous(a, sfa, b, sfb, grouped_layout, c=None, rows=None, cols=None):
     """M-grouped contiguous form ([likun] section 二, grouped_layout; [zwt] list).
 

@@ -302,6 +302,46 @@ def test_plain_definition_cross_check():
 
 
 # ----------------------------------------------------------------------------
+# storage layouts of the dense form (nt, nn, tn, tt)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+def test_layouts_brute_force_on_stored_arrays(layout):
+    # the brute force reads the stored arrays with the layout's own indexing
+    # (A[k][m] for "t", B[k][n] for a second "n"), independent of the
+    # transposition gemm_layout performs
+    rng = np.random.default_rng(40 + "nt nn tn tt".split().index(layout))
+    M, N, K = 6, 5, 256
+    a = _random_codes(rng, (M, K) if layout[0] == "n" else (K, M))
+    b = _random_codes(rng, (N, K) if layout[1] == "t" else (K, N))
+    sfa = rng.uniform(0.05, 3.0, size=(K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.05, 3.0, size=(1, K // 128)).astype(np.float32)
+    c = inputgen.bf16_bits_from_f32(rng.standard_normal((M, N)).astype(np.float32) * 20)
+    got = oracle.gemm_layout(layout, a, sfa, b, sfb, c)
+    for m in range(M):
+        for n in range(N):
+            tot = frac_bf16(int(c[m, n]))
+            for k in range(K):
+                av = frac_e4m3(int(a[m, k] if layout[0] == "n" else a[k, m])) * frac_f32(sfa[k // 128, m])
+                bv = frac_e4m3(int(b[n, k] if layout[1] == "t" else b[k, n])) * frac_f32(sfb[n // 128, k // 128])
+                tot += av * bv
+            assert int(got[m, n]) == frac_rne_bf16_bits(tot), (layout, m, n)
+
+
+def test_layouts_agree_on_transposed_storage():
+    # the same logical product stored four ways gives one result
+    rng = np.random.default_rng(44)
+    M, N, K = 9, 130, 384
+    a = _random_codes(rng, (M, K))
+    b = _random_codes(rng, (N, K))
+    sfa = rng.uniform(0.1, 2.0, size=(K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.1, 2.0, size=(2, K // 128)).astype(np.float32)
+    ref = oracle.gemm_nt(a, sfa, b, sfb)
+    stored = {"nt": (a, b), "nn": (a, b.T.copy()), "tn": (a.T.copy(), b.T.copy()), "tt": (a.T.copy(), b)}
+    for layout, (aa, bb) in stored.items():
+        assert np.array_equal(oracle.gemm_layout(layout, aa, sfa, bb, sfb), ref), layout
+
+
+# ----------------------------------------------------------------------------
 # grouped forms
 # ----------------------------------------------------------------------------
 def test_contiguous_brute_force_tiny():
