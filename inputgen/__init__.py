@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the FP8 block-scaled GEMM (NT) and its M-grouped forms.
+"""Seeded synthetic inputs for the FP8 block-scaled GEMM (NT), its M-grouped
+forms and the K-grouped TN form.
 
 This module is shared by the CPU oracle's tests, the GPU parity tests and the
 benchmark.  It holds no GEMM arithmetic: it draws random numbers, quantises
@@ -170,6 +171,33 @@ class Masked:
         return 2.0 * float(np.minimum(self.masked_m, self.max_m).sum()) * self.N * self.K
 
 
+@dataclass
+class KGrouped:
+    """K-grouped TN problem (MoE weight gradient): group g owns K rows
+    k_start[g] .. k_start[g+1]-1 of both operands (its tokens), ks[g] of them,
+    each a multiple of 128."""
+    a: np.ndarray            # [K][M] e4m3 codes, M contiguous (stored K-major)
+    sfa: np.ndarray          # [K/128][M] fp32, one per column m per 128 K rows
+    b: np.ndarray            # [K][N] e4m3 codes, N contiguous
+    sfb: np.ndarray          # [K/128][N] fp32, one per column n per 128 K rows
+    c: Optional[np.ndarray]  # [G][M][N] fp32 or None
+    ks: np.ndarray           # int32 [G], multiples of 128
+    counts: np.ndarray       # real tokens per group (<= ks)
+    M: int
+    N: int
+    K: int
+    G: int
+    name: str = "kgrouped"
+
+    @property
+    def k_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.ks)]).astype(np.int64)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * float(self.counts.sum()) * self.M * self.N
+
+
 # ----------------------------------------------------------------------------
 # random problems
 # ----------------------------------------------------------------------------
@@ -254,6 +282,37 @@ CONFIG_NAMES = [
 ]
 
 
+def make_kgrouped(G, M, N, total_tokens, seed=0, a_std=1.0, b_std=1.0, pow2=True, with_c=False,
+                  c_std=1.0, counts=None, name="kgrouped"):
+    """Draw order: counts (multinomial, equal probabilities, unless given), A, B, C.
+
+    Group g's tokens are padded to ks[g] = ceil(count/128)*128 K rows whose
+    padding holds zero codes and unit scales.  A is drawn as [tokens][M] and
+    quantised per column per 128 K rows (1x128 along K, the (1, 1, 128)
+    recipe); B likewise as [tokens][N]."""
+    rng = rng_for(seed)
+    if counts is None:
+        counts = rng.multinomial(total_tokens, [1.0 / G] * G)
+    counts = np.asarray(counts, dtype=np.int64)
+    ks = ((counts + BLOCK - 1) // BLOCK) * BLOCK
+    K = int(ks.sum())
+    real = np.zeros(K, dtype=bool)
+    off = 0
+    for g in range(G):
+        real[off:off + counts[g]] = True
+        off += ks[g]
+    xa = np.zeros((K, M), dtype=np.float32)
+    xa[real] = _normal(rng, (int(counts.sum()), M), a_std)
+    xb = np.zeros((K, N), dtype=np.float32)
+    xb[real] = _normal(rng, (int(counts.sum()), N), b_std)
+    # quantise along K: the transposed arrays are [M][K] rows with 1x128 blocks
+    ca, sfa = quantize_rows(np.ascontiguousarray(xa.T), pow2)
+    cb, sfb = quantize_rows(np.ascontiguousarray(xb.T), pow2)
+    c = _normal(rng, (G, M, N), c_std) if with_c else None
+    return KGrouped(np.ascontiguousarray(ca.T), sfa, np.ascontiguousarray(cb.T), sfb, c,
+                    ks.astype(np.int32), counts, M, N, K, G, name)
+
+
 def make_config(i: int, seed: int = 0):
     if i == 0:
         return make_dense(128, 256, 512, seed, 1.0, 1.0, None, True, CONFIG_NAMES[0])
@@ -293,6 +352,25 @@ def exact_dense(M, N, K, seed=0, e_min=-2, e_span=3, with_c=True, name="exact_de
     if with_c:
         c = bf16_bits_from_f32(rng.integers(-64, 65, size=(M, N)).astype(np.float32))
     return Dense(a, sfa, b, sfb, c, M, N, K, name)
+
+
+def exact_kgrouped(G, M, N, ks, seed=0, e_min=-2, e_span=3, with_c=True, name="exact_kgrouped"):
+    """K-grouped problem in the exact regime: integer codes in [-4, 4], scales
+    2**e with e in [e_min, e_min+e_span] per column per 128 K rows, C an integer
+    in [-64, 64] (fp32).  With every group's K below the exact_dense bound, every
+    fp32 partial sum, scale product and accumulation is exact."""
+    ks = np.asarray(ks, dtype=np.int32)
+    assert np.all(ks % BLOCK == 0) and np.all(ks >= 0)
+    assert int(ks.max(initial=0)) * 16 * (4 ** e_span) + 64 * 4 ** (-e_min) < 2 ** 24
+    rng = rng_for(seed)
+    K = int(ks.sum())
+    a = _int_codes(rng, (K, M))
+    b = _int_codes(rng, (K, N))
+    KB = K // BLOCK
+    sfa = np.ldexp(1.0, rng.integers(e_min, e_min + e_span + 1, size=(KB, M))).astype(np.float32)
+    sfb = np.ldexp(1.0, rng.integers(e_min, e_min + e_span + 1, size=(KB, N))).astype(np.float32)
+    c = rng.integers(-64, 65, size=(G, M, N)).astype(np.float32) if with_c else None
+    return KGrouped(a, sfa, b, sfb, c, ks, ks.astype(np.int64), M, N, K, G, name)
 
 
 def exact_subnormal_dense(M, N, K, seed=0, name="exact_subnormal"):

@@ -1,4 +1,5 @@
-"""CPU oracle for the FP8 block-scaled GEMM (NT) and its M-grouped MoE forms.
+"""CPU oracle for the FP8 block-scaled GEMM (NT and the nn/tn/tt storages), its
+M-grouped MoE forms and the K-grouped TN form.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The library's GPU path
@@ -17,4 +18,6 @@ from .fp8_gemm import (  # noqa: F401
     gemm_layout,
     m_grouped_contiguous,
     m_grouped_masked,
+    k_grouped_tn_acc,
+    k_grouped_tn,
 )

@@ -202,3 +202,52 @@ def m_grouped_masked(a, sfa, b, sfb, masked_m, c=None, groups=None, cols=None):
         out[i, :m] = gemm_nt(a[g][:m], sfa[g][:, :m], b[g], sfb[g], cg, None, cols)
         written[i, :m] = True
     return out, written
+
+
+def k_grouped_tn_acc(a, sfa, b, sfb, ks, c=None, groups=None):
+    """Unrounded fp64 results of the K-grouped TN form and their magnitudes.
+
+    [likun] section 一 lists a GEMM grouped along K ("k_grouped_fp8_gemm_tn",
+    for the MoE backward pass) and section 二 its call with per-group K sizes
+    (ks) and the (1, 1, 128) scale recipe.  Group g owns the K rows
+    k_start[g] .. k_start[g] + ks[g] - 1 of both operands; A is stored [K][M]
+    and B [K][N] (the "tn" storage); sfa[kb][m] and sfb[kb][n] scale one
+    column of one 128-row K block (1x128 along K for both operands).  Per group:
+
+        D[g][m][n] = C[g][m][n] + sum_kb sfa[kb][m] * sfb[kb][n]
+                                  * sum_{k in kb} dec(A[k][m]) * dec(B[k][n])
+
+    over the group's K blocks in ascending order, every step in fp64 (the
+    block sums are exact).  Returns (acc [G'][M][N], mag [G'][M][N]) where mag
+    is |C| plus the sum of the absolute values of every scaled product, the
+    scale against which an fp32 accumulation's rounding error is bounded."""
+    K, M = a.shape
+    N = b.shape[1]
+    ks = np.asarray(ks, dtype=np.int64)
+    assert b.shape[0] == K and sfa.shape == (K // BLOCK, M) and sfb.shape == (K // BLOCK, N)
+    assert np.all(ks % BLOCK == 0) and int(ks.sum()) == K
+    starts = np.concatenate([[0], np.cumsum(ks)])
+    groups = np.arange(len(ks)) if groups is None else np.asarray(groups)
+    acc = np.zeros((len(groups), M, N), dtype=np.float64)
+    mag = np.zeros((len(groups), M, N), dtype=np.float64)
+    for i, g in enumerate(groups):
+        for kb in range(int(starts[g]) // BLOCK, int(starts[g + 1]) // BLOCK):
+            rows = slice(kb * BLOCK, (kb + 1) * BLOCK)
+            A = decode_e4m3(a[rows])                         # [128][M]
+            B = decode_e4m3(b[rows])                         # [128][N]
+            s = sfa[kb].astype(np.float64)[:, None] * sfb[kb].astype(np.float64)[None, :]
+            acc[i] += s * (A.T @ B)                          # exact block sum, then scaled
+            mag[i] += np.abs(s) * (np.abs(A).T @ np.abs(B))
+        if c is not None:
+            cg = np.asarray(c)[g].astype(np.float64)
+            acc[i] += cg
+            mag[i] += np.abs(cg)
+    return acc, mag
+
+
+def k_grouped_tn(a, sfa, b, sfb, ks, c=None, groups=None):
+    """fp32 result of the K-grouped TN form (see k_grouped_tn_acc): each fp64
+    value rounded once to fp32, to nearest with ties to even."""
+    acc, _ = k_grouped_tn_acc(a, sfa, b, sfb, ks, c, groups)
+    return acc.astype(np.float32)
+

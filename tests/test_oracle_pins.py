@@ -55,6 +55,28 @@ def frac_rne_bf16_bits(x: Fraction) -> int:
     return sign | int(f32.view(np.uint32)[0] >> 16)
 
 
+def frac_rne_f32(x: Fraction) -> np.float32:
+    """Exact round-to-nearest-even of a rational to fp32 (normal range)."""
+    if x == 0:
+        return np.float32(0.0)
+    ax = -x if x < 0 else x
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    while Fraction(2) ** e > ax:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= ax:
+        e += 1
+    spacing_exp = max(e - 23, -149)
+    q = ax / (Fraction(2) ** spacing_exp)
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = Fraction(fl) * (Fraction(2) ** spacing_exp)
+    out = np.float32(float(val))            # val has <= 24 significant bits: exact
+    assert Fraction(float(out)) == val
+    return -out if x < 0 else out
+
+
 def frac_f32(v) -> Fraction:
     return Fraction(float(np.float32(v)))
 
@@ -339,6 +361,61 @@ def test_layouts_agree_on_transposed_storage():
     stored = {"nt": (a, b), "nn": (a, b.T.copy()), "tn": (a.T.copy(), b.T.copy()), "tt": (a.T.copy(), b)}
     for layout, (aa, bb) in stored.items():
         assert np.array_equal(oracle.gemm_layout(layout, aa, sfa, bb, sfb), ref), layout
+
+
+# ----------------------------------------------------------------------------
+# K-grouped TN form
+# ----------------------------------------------------------------------------
+def test_k_grouped_brute_force_tiny():
+    # exact rationals over the stored arrays (A[k][m], B[k][n], sfa[k//128][m],
+    # sfb[k//128][n]), group g summing only its own K rows, one rounding to fp32
+    rng = np.random.default_rng(51)
+    G, M, N = 3, 5, 4
+    ks = np.array([128, 0, 256], dtype=np.int32)
+    K = int(ks.sum())
+    a = _random_codes(rng, (K, M))
+    b = _random_codes(rng, (K, N))
+    sfa = rng.uniform(0.05, 3.0, size=(K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.05, 3.0, size=(K // 128, N)).astype(np.float32)
+    c = (rng.standard_normal((G, M, N)) * 30).astype(np.float32)
+    got = oracle.k_grouped_tn(a, sfa, b, sfb, ks, c)
+    assert got.dtype == np.float32 and got.shape == (G, M, N)
+    start = 0
+    for g in range(G):
+        for m in range(M):
+            for n in range(N):
+                tot = frac_f32(c[g, m, n])
+                for k in range(start, start + int(ks[g])):
+                    tot += (frac_e4m3(int(a[k, m])) * frac_f32(sfa[k // 128, m])
+                            * frac_e4m3(int(b[k, n])) * frac_f32(sfb[k // 128, n]))
+                assert got[g, m, n].view(np.uint32) == frac_rne_f32(tot).view(np.uint32), (g, m, n)
+        start += int(ks[g])
+    # an empty group gives C exactly; without C it gives zeros
+    assert np.array_equal(got[1], c[1])
+    assert not np.any(oracle.k_grouped_tn(a, sfa, b, sfb, ks)[1])
+
+
+def test_k_grouped_exact_regime_closed_form():
+    # integer codes and power-of-two scales: Python integers (scaled by the
+    # smallest scale product) give the exact value, which fp32 holds exactly
+    p = inputgen.exact_kgrouped(3, 16, 32, [256, 128, 0], seed=5, e_min=-2, e_span=3)
+    got = oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c)
+    ia = oracle_free_int_values(p.a).astype(np.int64)            # [K][M]
+    ib = oracle_free_int_values(p.b).astype(np.int64)            # [K][N]
+    ea = np.log2(p.sfa).astype(np.int64)                         # [KB][M]
+    eb = np.log2(p.sfb).astype(np.int64)
+    unit = 2 * -2                                                # exponent of the smallest scale product
+    start = 0
+    for g in range(p.G):
+        tot = (p.c[g].astype(np.int64) << (-unit))               # C in units of 2**unit
+        for k in range(start, start + int(p.ks[g])):
+            kb = k // 128
+            sh = ea[kb][:, None] + eb[kb][None, :] - unit        # >= 0
+            tot = tot + ((ia[k][:, None] * ib[k][None, :]) << sh)
+        start += int(p.ks[g])
+        exact = tot.astype(np.float64) * 2.0 ** unit
+        assert np.array_equal(got[g], exact.astype(np.float32)), g
+        assert np.all(np.abs(tot) < 2 ** 53)
 
 
 # ----------------------------------------------------------------------------
