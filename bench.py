@@ -3,13 +3,13 @@
 One step is one library call over one batch of synthetic inputs already
 resident in HBM.  The headline workload is the dense decode shape
 M=64 N=2112 K=7168 (A ~ N(0,1), B ~ N(0,0.02), 1x128 / 128x128 power-of-two
-scales, bf16 C ~ N(0,0.1)); the other four workloads, and the prefill problem
-with K-major operands (nn, tn, tt), are reported per shape in the same JSON
-line.  Inputs rotate over enough copies that successive steps
+scales, bf16 C ~ N(0,0.1)); the other four workloads, the prefill problem
+with K-major operands (nn, tn, tt) and a K-grouped TN (MoE weight-gradient)
+problem are reported per shape in the same JSON line.  Inputs rotate over enough copies that successive steps
 read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5,6,7,8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5,6,7,8,9]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
 
@@ -50,6 +50,9 @@ SHAPES = {
     6: ("dense_prefill_4096x7168x16384_nn", "mfma"),
     7: ("dense_prefill_4096x7168x16384_tn", "mfma"),
     8: ("dense_prefill_4096x7168x16384_tt", "mfma"),
+    # K-grouped TN (MoE weight gradient): 8 experts, M=4096 x N=7168 per expert,
+    # 8192 tokens split multinomially, fp32 D
+    9: ("kgrouped_tn_8x4096x7168_tokens8192", "mfma"),
 }
 LAYOUT_OF = {6: "nn", 7: "tn", 8: "tt"}
 PROBLEM_OF = {6: 3, 7: 3, 8: 3}        # workload index whose generated problem a layout entry reuses
@@ -110,6 +113,9 @@ def algorithmic_bytes(p) -> int:
         used = np.unique(p.grouped_layout[p.grouped_layout >= 0])
         b = sum(p.b[g].nbytes + p.sfb[g].nbytes for g in used)
         return rows * p.K + rows * KB * 4 + rows * 4 + b + rows * p.N * 2
+    if isinstance(p, inputgen.KGrouped):
+        tokens = int(p.counts.sum())
+        return tokens * (p.M + p.N) + (tokens // 128 + p.G) * (p.M + p.N) * 4 + p.G * p.M * p.N * 4
     if isinstance(p, inputgen.Masked):
         m = np.minimum(np.maximum(p.masked_m, 0), p.max_m)
         rows = int(m.sum())
@@ -124,7 +130,10 @@ class Workload:
     def __init__(self, idx, torch, dg, copies=None):
         import inputgen
         t0 = time.time()
-        self.p = p = inputgen.make_config(PROBLEM_OF.get(idx, idx) - 1, seed=0)
+        if idx == 9:
+            self.p = p = inputgen.make_kgrouped(8, 4096, 7168, 8192, seed=0, name=SHAPES[idx][0])
+        else:
+            self.p = p = inputgen.make_config(PROBLEM_OF.get(idx, idx) - 1, seed=0)
         self.name, self.bound = SHAPES[idx]
         self.layout = LAYOUT_OF.get(idx, "nt")
         self.flops = p.flops
@@ -152,6 +161,9 @@ class Workload:
             elif isinstance(p, inputgen.Contiguous):
                 s["layout"] = up(p.grouped_layout)
                 s["d"] = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+            elif isinstance(p, inputgen.KGrouped):
+                # fp32 D [G][M][N] is large: every copy writes the same buffer
+                s["d"] = self.sets[0]["d"] if i else torch.empty((p.G, p.M, p.N), dtype=torch.float32, device=dev)
             else:
                 s["masked_m"] = up(p.masked_m)
                 s["d"] = torch.empty((p.G, p.max_m, p.N), dtype=torch.bfloat16, device=dev)
@@ -166,6 +178,8 @@ class Workload:
         dg = self.dg
         if self.kind == "Dense":
             getattr(dg, "dg_fp8_gemm_" + self.layout)(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
+        elif self.kind == "KGrouped":
+            dg.dg_k_grouped_fp8_gemm_tn_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"], self.p.ks)
         elif self.kind == "Contiguous":
             dg.dg_m_grouped_fp8_gemm_nt_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"], s["layout"])
         else:
@@ -232,7 +246,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8", help="comma-separated 1-based workload indices")
+    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")

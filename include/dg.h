@@ -114,6 +114,30 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void*
                                     int K, int num_groups, const int32_t* masked_m,
                                     int expected_m, void* stream);
 
+/* K-grouped GEMM, TN layout, for MoE weight gradients (likun.im section 一:
+ * "k_grouped_fp8_gemm_tn", grouped along K for the MoE backward pass; section
+ * 二: the call takes the per-group K sizes ks and the (1, 1, 128) scale
+ * recipe).  Group g owns K rows k_start[g] .. k_start[g] + ks[g] - 1 of both
+ * operands (k_start = running sum of ks), i.e. its tokens, and
+ *   D[g][m][n] = C[g][m][n] + sum_kb sfa[kb][m] * sfb[kb][n]
+ *                             * sum_{k in block kb} A[k][m] * B[k][n]
+ * over the group's 128-row K blocks, accumulated in fp32 and stored in fp32.
+ *   a    uint8  [K][M]   e4m3 codes, M contiguous (16-byte aligned)
+ *   sfa  float  [K/128][M]   one scale per column per 128 K rows
+ *   b    uint8  [K][N]   e4m3 codes, N contiguous (16-byte aligned)
+ *   sfb  float  [K/128][N]   one scale per column per 128 K rows
+ *   c    float  [G][M][N] or NULL (C = 0); may equal d (accumulation)
+ *   d    float  [G][M][N] output (a group with ks[g] == 0 gets C, or zeros)
+ *   ks   int32  [num_groups] on the HOST: each a non-negative multiple of 128
+ *        (pad a group's tokens with zero rows); K = sum of ks.
+ * M and N must be multiples of 16 and num_groups at most 256
+ * (DG_ERR_UNSUPPORTED otherwise).  The K offsets travel in the launch's
+ * arguments, so a captured graph replays the call with the ks it was captured
+ * with.  Returns a dg_status. */
+int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* sfa, const void* b,
+                                        const float* sfb, const float* c, float* d, int M, int N,
+                                        int num_groups, const int32_t* ks, void* stream);
+
 /* Prepares per-device state for the current HIP device (device properties and
  * the split-K workspace, allocated once and kept until the process ends).
  * Calls above do this lazily on first use; call dg_init() first when the

@@ -1,5 +1,5 @@
 """FP8 (e4m3) block-scaled GEMM (NT, and NN/TN/TT with K-major operands), with
-M-grouped MoE forms, for AMD MI355X (gfx950).  The kernels live in libdg.so behind the C ABI of
+M-grouped MoE forms and the K-grouped TN form, for AMD MI355X (gfx950).  The kernels live in libdg.so behind the C ABI of
 include/dg.h; this package is its Python binding."""
 from ._lib import (  # noqa: F401
     DGError,
@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     dg_fp8_gemm_tn,
     dg_fp8_gemm_tt,
     dg_init,
+    dg_k_grouped_fp8_gemm_tn_contiguous,
     dg_m_grouped_fp8_gemm_nt_contiguous,
     dg_m_grouped_fp8_gemm_nt_masked,
     dg_version,

@@ -26,6 +26,7 @@ EXPORTED = [
     "dg_fp8_gemm_tt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
+    "dg_k_grouped_fp8_gemm_tn_contiguous",
     "dg_init",
     "dg_last_error",
     "dg_version",
@@ -58,6 +59,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
         lib.dg_m_grouped_fp8_gemm_nt_masked.restype = ci
+        lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp, vp]
+        lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = ci
         lib.dg_init.argtypes = []
         lib.dg_init.restype = ci
         lib.dg_last_error.argtypes = []
@@ -167,3 +170,16 @@ def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, c, d, masked_m, expected_m, 
         _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
         _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), max_m, N, K, G,
         _ptr(masked_m, "masked_m", (torch.int32,)), int(expected_m), _stream(stream)))
+
+
+def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, c, d, ks, stream=None) -> None:
+    """K-grouped TN form: a [K][M], b [K][N], sfa [K/128][M], sfb [K/128][N], c and d fp32
+    [G][M][N]; ks is a host sequence of per-group K sizes (multiples of 128)."""
+    K, M = a.shape
+    N = b.shape[1]
+    ks_host = (ctypes.c_int32 * len(ks))(*[int(k) for k in ks])
+    _check("dg_k_grouped_fp8_gemm_tn_contiguous", load().dg_k_grouped_fp8_gemm_tn_contiguous(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
+        _ptr(c, "c", (torch.float32,), True), _ptr(d, "d", (torch.float32,)), M, N, len(ks),
+        ctypes.cast(ks_host, ctypes.c_void_p), _stream(stream)))

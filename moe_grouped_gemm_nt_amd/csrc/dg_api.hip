@@ -302,6 +302,65 @@ extern "C" int dg_fp8_gemm_tt(const void* a, const float* sfa, const void* b, co
   return dense_kmajor(a, sfa, b, sfb, c, d, M, N, K, 1, stream);
 }
 
+extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* sfa, const void* b,
+                                                   const float* sfb, const float* c, float* d, int M, int N,
+                                                   int num_groups, const int32_t* ks, void* stream) {
+  if (!a || !sfa || !b || !sfb || !d || !ks)
+    return fail(DG_ERR_INVALID_ARG, "a, sfa, b, sfb, d and ks must not be NULL");
+  if (M < 0 || N < 0) return fail(DG_ERR_INVALID_ARG, "negative size (M=%d N=%d)", M, N);
+  if (num_groups < 1) return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be at least 1", num_groups);
+  if (num_groups > dg::kMaxKGroups)
+    return fail(DG_ERR_UNSUPPORTED, "num_groups=%d exceeds %d", num_groups, dg::kMaxKGroups);
+  if (!aligned(a, 16) || !aligned(b, 16)) return fail(DG_ERR_INVALID_ARG, "a and b must be 16-byte aligned");
+  if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(d, 4) || (c && !aligned(c, 4)))
+    return fail(DG_ERR_INVALID_ARG, "sfa, sfb, c and d must be 4-byte aligned");
+  dg::KGroupedParams p{};
+  long long K = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks[g] < 0 || ks[g] % 128 != 0)
+      return fail(DG_ERR_INVALID_ARG, "ks[%d]=%d is not a non-negative multiple of 128", g, ks[g]);
+    p.k_start[g] = (int)K;
+    K += ks[g];
+    if (K > (1LL << 30)) return fail(DG_ERR_UNSUPPORTED, "total K of %lld is too large", K);
+  }
+  p.k_start[num_groups] = (int)K;
+  if (M % 16 != 0 || N % 16 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "the K-major operands need M and N multiples of 16 (M=%d N=%d)", M, N);
+  if (M == 0 || N == 0) return DG_OK;
+  DeviceState* st = nullptr;
+  int s = get_device_state(&st);
+  if (s != DG_OK) return s;
+  if ((long long)N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", N);
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.d32 = d;
+  p.c32 = c;
+  p.rows = M;
+  p.N = N;
+  p.K = (int)K;
+  p.G = num_groups;
+  p.splits = 1;
+  // the largest tile that still gives every CU a work item (as for dense calls)
+  const long long t256 = (long long)num_groups * ((M + 255) / 256) * ((N + 255) / 256);
+  const long long t128x256 = (long long)num_groups * ((M + 127) / 128) * ((N + 255) / 256);
+  int cfg = t256 >= st->num_cus ? dg::kCfg256x256w8 : t128x256 >= st->num_cus ? dg::kCfg128x256w8 : dg::kCfg128x128;
+  const int forced = env_int("DG_FORCE_CONFIG", -1);
+  if (forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 || forced == dg::kCfg256x256w8) cfg = forced;
+  const dg::ConfigInfo& ci = dg::config_info(cfg);
+  p.tiles_m = (M + ci.bm - 1) / ci.bm;
+  p.tiles_n = (N + ci.bn - 1) / ci.bn;
+  const long long items = (long long)num_groups * p.tiles_m * p.tiles_n;
+  if (items > (1LL << 30)) return fail(DG_ERR_UNSUPPORTED, "problem too large (%lld work items)", items);
+  const int grid = (int)(((items + 7) / 8) * 8);
+  if (env_int("DG_LOG", 0))
+    std::fprintf(stderr, "[dg] k-grouped M=%d N=%d K=%lld G=%d cfg=%s grid=%d\n", M, N, K, num_groups, ci.name, grid);
+  hipError_t e = dg::launch_kgrouped(cfg, p, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return DG_OK;
+}
+
 extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
                                                    const float* sfb, const void* c, void* d, int M,
                                                    int N, int K, int num_groups,

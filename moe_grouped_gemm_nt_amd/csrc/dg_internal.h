@@ -7,7 +7,8 @@
 
 namespace dg {
 
-enum Mode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kKGrouped: groups along K (each group's tokens), both operands K-major, fp32 D.
+enum Mode : int { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 
 // Everything one launch needs.  Row counts and strides are in elements.
 struct Params {
@@ -31,6 +32,15 @@ struct Params {
   int splits;              // split-K factor (>= 1; decode kernel only)
   int kbs_per_split;       // K blocks per split (decode kernel only)
   int ab_layout;           // dense: bit 0 = A stored [K][M], bit 1 = B stored [K][N] (0 = nt)
+  float* d32;              // K-grouped: fp32 D [G][M][N]
+  const float* c32;        // K-grouped: fp32 C [G][M][N] or nullptr
+};
+
+// The K-grouped form carries its groups' K offsets in the launch arguments,
+// so a captured graph replays with the offsets of the captured call.
+constexpr int kMaxKGroups = 256;
+struct KGroupedParams : Params {
+  int k_start[kMaxKGroups + 1];   // group g owns K rows k_start[g] .. k_start[g+1]-1 (multiples of 128)
 };
 
 // Tile configurations compiled into the library.
@@ -62,6 +72,8 @@ const ConfigInfo& config_info(int cfg);
 // persistently when grid is smaller than the tile count; the decode
 // configuration sizes its own grid from tiles and splits.
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
+// K-grouped TN launch on configuration cfg (128x128, 128x256 or 256x256 tiles).
+hipError_t launch_kgrouped(int cfg, const KGroupedParams& p, int grid, hipStream_t stream);
 
 // Power-of-two-scale kernels (fp8_gemm_e8m0.hip).  Launched with a gate
 // (Params::gate_ok) after launch_scale_check, beside the general kernel with

@@ -399,6 +399,24 @@ const ConfigInfo kConfigs[kNumConfigs] = {
 
 const ConfigInfo& config_info(int cfg) { return kConfigs[cfg]; }
 
+namespace {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
+hipError_t launch_kg_cfg(const KGroupedParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, kKGrouped, 1, false, 3, KGroupedParams>),
+                     dim3(grid), dim3(WAVES_M * WAVES_N * 64), 0, stream, p);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kgrouped(int cfg, const KGroupedParams& p, int grid, hipStream_t stream) {
+  switch (cfg) {
+    case kCfg128x128: return launch_kg_cfg<128, 128, 2, 2, 4>(p, grid, stream);
+    case kCfg128x256w8: return launch_kg_cfg<128, 256, 2, 4, 3>(p, grid, stream);
+    case kCfg256x256w8: return launch_kg_cfg<256, 256, 2, 4, 2>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream) {
   switch (cfg) {
     case kCfg128x128: return launch_cfg<128, 128, 2, 2, 4>(mode, p, grid, stream);

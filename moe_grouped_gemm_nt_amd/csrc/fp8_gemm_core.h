@@ -247,7 +247,9 @@ __device__ __forceinline__ v8i kmajor_frag(uint32_t addr) {
 // ============================================================================
 // prefill / grouped kernel
 // ============================================================================
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT>
+// CS: B scales per column per K block (the K-grouped form) instead of one per
+// 128x128 block: each wave loads 64 of them per block into its own area.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, bool CS = false>
 struct Shape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -268,10 +270,16 @@ struct Shape {
   // LDS: [A slot 0..NSLOT-1][B slot 0..NSLOT-1][scales slot 0..NSLOT-1]
   static constexpr int B_REGION = NSLOT * A_BYTES;
   static constexpr int S_REGION = NSLOT * (A_BYTES + B_BYTES);
-  static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
+  // column scales (CS): wave w's 64 floats hold columns 64*(w % (BN/64)) ..
+  // +63, so column x of the tile sits at float x of the area
+  static constexpr bool HAS_CS = CS;
+  static constexpr int SC_BYTES = CS ? NWAVES * 256 : 0;
+  static constexpr int SC_REGION = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
+  static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES + SC_BYTES);
   static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
   static constexpr int B_INSTR = BN / 8 / NWAVES;
-  static constexpr int LPS = A_INSTR + B_INSTR + 1 + SB_SEP;   // loads per wave per K block
+  static constexpr int LPS = A_INSTR + B_INSTR + 1 + SB_SEP + CS;   // loads per wave per K block
+  static_assert(!CS || (BN % 64 == 0 && BN / 64 <= NWAVES), "column scales: one 64-column load per wave");
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves per workgroup");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must sit in one 128-wide B scale block");
@@ -310,12 +318,19 @@ __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32
 // LAYOUT: bit 0 set = A is stored K-major ([K][M], M contiguous: the "t" of
 //         "tn"/"tt"), bit 1 set = B is stored [K][N] (the second "n" of
 //         "nn"/"tn"); clear bits are the K-contiguous "nt" operands.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU, bool E8M0, int LAYOUT = 0>
+// MODE kKGrouped (PT = KGroupedParams): work items are (group, tile) pairs;
+// group g's K range is k_start[g] .. k_start[g+1]-1, both operands K-major,
+// B scales per column, fp32 D and C.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_PER_CU, bool E8M0, int LAYOUT = 0,
+          class PT = Params>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WG_PER_CU)
-fp8_gemm_nt_kernel(Params p) {
-  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT>;
+fp8_gemm_nt_kernel(PT p) {
+  constexpr bool KG = MODE == kKGrouped;
+  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT, KG>;
   constexpr bool TA = (LAYOUT & 1) != 0, TB = (LAYOUT & 2) != 0;
-  static_assert(LAYOUT == 0 || MODE == kDense, "K-major operands are supported by the dense form");
+  static_assert(LAYOUT == 0 || MODE == kDense || (KG && LAYOUT == 3),
+                "K-major operands are supported by the dense and K-grouped forms");
+  static_assert(!KG || (LAYOUT == 3 && !E8M0), "the K-grouped form reads K-major operands with fp32 promotion");
   static_assert((!TA || S::WTM % 32 == 0) && (!TB || S::WTN % 32 == 0), "K-major strips pair up in 32-row steps");
   // Path gate: the scale check kernel leaves one verdict per check workgroup;
   // the E8M0 kernel runs only if all scales are powers of two, the other
@@ -363,6 +378,8 @@ fp8_gemm_nt_kernel(Params p) {
   const uint32_t offS0 = smem_base + S::S_REGION +
                          4 * (((wrow0 + g16 * 4) / S::RS) * S::SA_PER_WAVE + (wrow0 + g16 * 4) % S::RS);
   const uint32_t offSB = smem_base + S::S_REGION + 4 * (wave * S::SA_PER_WAVE + S::RS);
+  // K-grouped: column scale of the lane's column in strip 0 (strip j adds 64 bytes)
+  const uint32_t offSC = smem_base + S::SC_REGION + 4 * (wcol0 + r16);
   // scale of the lane's MFMA operand row (row 16*i + l%16 of the wave tile) in strip 0
   const uint32_t offR0 = smem_base + S::S_REGION +
                          4 * (((wrow0 + r16) / S::RS) * S::SA_PER_WAVE + (wrow0 + r16) % S::RS);
@@ -383,6 +400,8 @@ fp8_gemm_nt_kernel(Params p) {
     }
     __syncthreads();
     total = s_prefix[p.G];
+  } else if constexpr (KG) {
+    total = p.G * p.tiles_m * p.tiles_n;
   } else {
     total = p.tiles_m * p.tiles_n;
   }
@@ -414,7 +433,13 @@ fp8_gemm_nt_kernel(Params p) {
       nt = local / tm;
       rows_lim = m;
     } else {
-      tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
+      if constexpr (KG) {
+        const int per_group = p.tiles_m * p.tiles_n;
+        group = w / per_group;
+        tile_coords(w - group * per_group, p.tiles_m, p.tiles_n, mt, nt);
+      } else {
+        tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
+      }
       if constexpr (MODE == kContiguous) {
         // the expert of each 128-row block of the tile: the largest id among
         // its rows (padding rows may carry -1); all valid ids in a block agree
@@ -447,7 +472,11 @@ fp8_gemm_nt_kernel(Params p) {
 
     const int m0 = mt * BM;
     const int n0 = nt * BN;
-    const int kbs = KB;
+    int kbs = KB, kb0 = 0;          // this item's K blocks (K-grouped: the group's)
+    if constexpr (KG) {
+      kb0 = p.k_start[group] / KBLK;
+      kbs = p.k_start[group + 1] / KBLK - kb0;
+    }
 
     // ---- operand bases -----------------------------------------------------
     const uint8_t* A = p.a;
@@ -463,11 +492,22 @@ fp8_gemm_nt_kernel(Params p) {
       D += (size_t)group * p.rows * p.N;
       if (C) C += (size_t)group * p.rows * p.N;
     }
-    if constexpr (MODE != kDense) {
+    if constexpr (MODE == kContiguous || MODE == kMasked) {
       B += (size_t)group * p.N * p.K;
       SB += (size_t)group * NB * KB;
     }
-    int nb = (n0 + wcol0) / 128;
+    float* D32 = nullptr;
+    const float* C32 = nullptr;
+    if constexpr (KG) {
+      // the group's first K row of A [K][M] and B [K][N] and of the scales
+      A += (size_t)kb0 * KBLK * a_rows;
+      B += (size_t)kb0 * KBLK * p.N;
+      SA += (size_t)kb0 * a_rows;
+      SB += (size_t)kb0 * p.N;          // column scales [K/128][N]
+      D32 = p.d32 + (size_t)group * a_rows * p.N;
+      if (p.c32) C32 = p.c32 + (size_t)group * a_rows * p.N;
+    }
+    int nb = KG ? 0 : (n0 + wcol0) / 128;
     nb = nb < NB ? nb : NB - 1;
 
     // ---- load addresses -------------------------------------------------------
@@ -523,10 +563,14 @@ fp8_gemm_nt_kernel(Params p) {
       s_src = SB + (size_t)nb * KB;
       s_stride = 1;
     }
+    // K-grouped: this wave's 64 column scales of each K block
+    const float* sc_src = SB + min(n0 + 64 * (wave % (BN / 64)) + lane, p.N - 1);
 
     // the k-th load instruction (k < LPS) of K block i into slot u
     auto issue_one = [&](int k, int i, int u) {
-      if (k < S::A_INSTR) {
+      if (S::HAS_CS && k == S::LPS - 1) {
+        dma_4(sc_src + (size_t)i * p.N, smem_base + S::SC_REGION + u * S::SC_BYTES + wave * 256);
+      } else if (k < S::A_INSTR) {
         dma_16s(a_tile + i * a_kstep, a_off[k], smem_base + u * S::A_BYTES + (wave + S::NWAVES * k) * 1024);
       } else if (k < S::A_INSTR + S::B_INSTR) {
         const int j = k - S::A_INSTR;
@@ -556,7 +600,8 @@ fp8_gemm_nt_kernel(Params p) {
     // the vector-memory queue drains while the matrix cores run.
     auto compute = [&](auto u_const, int next, int next_u, float live) {
       constexpr int u = decltype(u_const)::value;
-      const float sb = lds_f32(offSB + u * S::S_BYTES) * live;
+      // the block's B scale (K-grouped: 1, the per-column scales enter below)
+      const float sb = KG ? live : lds_f32(offSB + u * S::S_BYTES) * live;
       auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) {
         const v4i lo = lds_v4i(lo_addr), hi = lds_v4i(hi_addr);
         return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -607,6 +652,9 @@ fp8_gemm_nt_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < S::SN; ++j)
         bf[j] = fragB(j);
+      float sbc[S::SN];               // K-grouped: the lane's column scale in each column strip
+#pragma unroll
+      for (int j = 0; j < S::SN; ++j) sbc[j] = KG ? lds_f32(offSC + j * 64 + u * S::SC_BYTES) : 1.f;
       // A strips are read one strip ahead of their MFMAs, which bounds the live
       // A fragments to two
       auto load_strip = [&](int i) {
@@ -634,7 +682,7 @@ fp8_gemm_nt_kernel(Params p) {
         if (v >= 0) {
           v4f& a = acc[v / S::SN][v % S::SN];
           const v4f& q = part[v % P];
-          const v4f& c = sc[v / S::SN];
+          const v4f c = KG ? sc[v / S::SN] * sbc[v % S::SN] : sc[v / S::SN];
           a.x = __builtin_fmaf(q.x, c.x, a.x);
           a.y = __builtin_fmaf(q.y, c.y, a.y);
           a.z = __builtin_fmaf(q.z, c.z, a.z);
@@ -698,10 +746,16 @@ fp8_gemm_nt_kernel(Params p) {
           const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
           const int col = n0 + wcol0 + j * 16 + r16;
           float v = acc[i][j][e];
-          if (C) v += bf16_to_f32(C[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
-          if (row < rows_lim && col < p.N &&
-              (MODE != kContiguous || p.layout[min(row, p.rows - 1)] == group))
-            D[(size_t)row * p.N + col] = f32_to_bf16(v);
+          if constexpr (KG) {
+            // fp32 result: + C, no rounding beyond the fp32 accumulation
+            if (C32) v += C32[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)];
+            if (row < rows_lim && col < p.N) D32[(size_t)row * p.N + col] = v;
+          } else {
+            if (C) v += bf16_to_f32(C[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
+            if (row < rows_lim && col < p.N &&
+                (MODE != kContiguous || p.layout[min(row, p.rows - 1)] == group))
+              D[(size_t)row * p.N + col] = f32_to_bf16(v);
+          }
         }
     // the next item reuses the LDS ring; nothing of this item stays in flight
     // (without this the compiler assumes a load of this item may still be
