@@ -67,6 +67,42 @@ def encode_e4m3(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+E2M1_MAX = 6.0
+_E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def encode_e2m1(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP E2M1 (FP4) codes 0..15, round to nearest with ties to the
+    even code (even mantissa bit), saturating at +-6."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.minimum(np.abs(x), E2M1_MAX)
+    # distances to the 8 magnitudes; ties go to the even code
+    d = np.abs(mag[..., None] - _E2M1_VALUES)
+    best = np.argmin(d + 1e-9 * (np.arange(8) % 2), axis=-1)   # prefer even codes on ties
+    code = best.astype(np.uint8)
+    code[(x < 0) & (code != 0)] |= 8
+    return code
+
+
+def quantize_fp4_rows(x: np.ndarray):
+    """1x32 FP4 quantisation of x [N][K] with E8M0 scales: per row per 32 K
+    values, scale = 2**ceil(log2(amax/6)) (1 for an all-zero group), code =
+    RNE_e2m1(x / scale).  Returns (packed codes [N][K/2] u8, element 2i in the
+    low nibble, scale exponents [N][K/32] as biased E8M0 bytes)."""
+    N, K = x.shape
+    assert K % 32 == 0
+    xb = x.reshape(N, K // 32, 32).astype(np.float32)
+    amax = np.abs(xb).max(axis=2)
+    e = np.zeros_like(amax, dtype=np.int64)
+    nz = amax > 0
+    # smallest e with 6 * 2**e >= amax, exactly via frexp of amax / 6 in fp64
+    m, ex = np.frexp(amax[nz].astype(np.float64) / E2M1_MAX)
+    e[nz] = np.where(m == 0.5, ex - 1, ex)
+    codes = encode_e2m1(xb / np.ldexp(1.0, e)[:, :, None]).reshape(N, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
@@ -169,6 +205,36 @@ class Masked:
     @property
     def flops(self) -> float:
         return 2.0 * float(np.minimum(self.masked_m, self.max_m).sum()) * self.N * self.K
+
+
+@dataclass
+class DenseFP4:
+    """FP8 x FP4 dense problem: A e4m3 with 1x128 fp32 scales as in Dense; B
+    holds OCP E2M1 codes two to a byte (element 2i in the low nibble) with one
+    E8M0 scale per row per 32 K values, packed four to an int32 in K order."""
+    a: np.ndarray            # [M][K] e4m3 codes
+    sfa: np.ndarray          # [K/128][M] fp32
+    b: np.ndarray            # [N][K/2] packed E2M1
+    sfb: np.ndarray          # [K/128][N] int32: byte j = E8M0 of K values 32j..32j+31 of the block
+    c: Optional[np.ndarray]  # [M][N] bf16 bits or None
+    M: int
+    N: int
+    K: int
+    name: str = "dense_fp4"
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+def pack_e8m0_blocks(e: np.ndarray) -> np.ndarray:
+    """E8M0 bytes [N][K/32] -> int32 [K/128][N], byte j of an int holding the
+    scale of K values 32j..32j+31 of that 128-wide block."""
+    N, KS = e.shape
+    assert KS % 4 == 0
+    q = e.reshape(N, KS // 4, 4).astype(np.uint32)
+    packed = q[:, :, 0] | (q[:, :, 1] << 8) | (q[:, :, 2] << 16) | (q[:, :, 3] << 24)
+    return np.ascontiguousarray(packed.T).view(np.int32)
 
 
 @dataclass
@@ -311,6 +377,37 @@ def make_kgrouped(G, M, N, total_tokens, seed=0, a_std=1.0, b_std=1.0, pow2=True
     c = _normal(rng, (G, M, N), c_std) if with_c else None
     return KGrouped(np.ascontiguousarray(ca.T), sfa, np.ascontiguousarray(cb.T), sfb, c,
                     ks.astype(np.int32), counts, M, N, K, G, name)
+
+
+def make_dense_fp4(M, N, K, seed=0, a_std=1.0, b_std=1.0, c_std=None, pow2=True, name="dense_fp4"):
+    """Draw order: A, B, C.  A as in make_dense; B quantised to FP4 per row per 32."""
+    rng = rng_for(seed)
+    a, sfa = quantize_rows(_normal(rng, (M, K), a_std), pow2)
+    b, e = quantize_fp4_rows(_normal(rng, (N, K), b_std))
+    c = bf16_bits_from_f32(_normal(rng, (M, N), c_std)) if c_std is not None else None
+    return DenseFP4(a, sfa, b, pack_e8m0_blocks(e), c, M, N, K, name)
+
+
+def exact_dense_fp4(M, N, K, seed=0, e_min=-2, e_span=2, with_c=True, name="exact_dense_fp4"):
+    """FP8 x FP4 problem in the exact regime: A integer codes in [-4, 4] with
+    scales 2**e (e in [e_min, e_min+e_span]); B codes from every E2M1 value
+    (multiples of 1/2, |b| <= 6) with E8M0 scales 2**e, e in the same range;
+    C an integer in [-64, 64].  Every scaled product is a multiple of
+    2**(2*e_min - 1) of at most 48 * 4**e_span such units, so with
+    K*48*4**e_span + 64*2**(1 - 2*e_min) < 2**24 every fp32 partial sum,
+    promotion and accumulation is exact in any order."""
+    assert K * 48 * 4 ** e_span + 64 * 2 ** (1 - 2 * e_min) < 2 ** 24
+    rng = rng_for(seed)
+    a = _int_codes(rng, (M, K))
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    b = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    KB = K // BLOCK
+    sfa = np.ldexp(1.0, rng.integers(e_min, e_min + e_span + 1, size=(KB, M))).astype(np.float32)
+    e = (rng.integers(e_min, e_min + e_span + 1, size=(N, K // 32)) + 127).astype(np.uint8)
+    c = None
+    if with_c:
+        c = bf16_bits_from_f32(rng.integers(-64, 65, size=(M, N)).astype(np.float32))
+    return DenseFP4(a, sfa, b, pack_e8m0_blocks(e), c, M, N, K, name)
 
 
 def make_config(i: int, seed: int = 0):

@@ -1,5 +1,5 @@
 """CPU oracle for the FP8 block-scaled GEMM (NT and the nn/tn/tt storages), its
-M-grouped MoE forms and the K-grouped TN form.
+M-grouped MoE forms, the K-grouped TN form and the FP8 x FP4 GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The library's GPU path
@@ -20,4 +20,10 @@ from .fp8_gemm import (  # noqa: F401
     m_grouped_masked,
     k_grouped_tn_acc,
     k_grouped_tn,
+)
+from .fp8_fp4 import (  # noqa: F401
+    E2M1_VALUES,
+    decode_e2m1_packed,
+    gemm_fp8_fp4_nt_acc,
+    gemm_fp8_fp4_nt,
 )

@@ -486,3 +486,61 @@ def test_golden_closed_form_fixtures():
         got = _dec_bits(oracle.gemm_nt(a, sfa, b, sfb, c))
         for (m, n), v in case["expect"]:
             assert got[m, n] == v, (case["name"], m, n, got[m, n], v)
+
+
+# ----------------------------------------------------------------------------
+# FP8 x FP4 form
+# ----------------------------------------------------------------------------
+def test_e2m1_table_against_the_format_value_list():
+    # OCP Microscaling Formats v1.0, FP4 (E2M1) element data type: the eight
+    # magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6; the top bit is the sign
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(oracle.E2M1_VALUES[:8]) == mags
+    assert list(oracle.E2M1_VALUES[8:]) == [-m for m in mags]
+
+
+def _nibble(b, n, k):
+    byte = int(b[n, k // 2])
+    return (byte >> 4) if k % 2 else (byte & 0xF)
+
+
+def frac_e2m1(code: int) -> Fraction:
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+    return -mags[code & 7] if code & 8 else mags[code & 7]
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(3, 5, 128, 60), (4, 3, 256, 61)])
+def test_fp8_fp4_brute_force_tiny(M, N, K, seed):
+    # exact rationals from the stored arrays: nibbles of b, the E8M0 byte of
+    # each 32 K values taken from the packed int, one rounding to bf16
+    rng = np.random.default_rng(seed)
+    a = _random_codes(rng, (M, K))
+    b = rng.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+    sfa = rng.uniform(0.05, 3.0, size=(K // 128, M)).astype(np.float32)
+    ebytes = rng.integers(120, 135, size=(K // 128, N, 4)).astype(np.uint32)
+    sfb = (ebytes[..., 0] | (ebytes[..., 1] << 8) | (ebytes[..., 2] << 16) | (ebytes[..., 3] << 24)).view(np.int32)
+    c = inputgen.bf16_bits_from_f32(rng.standard_normal((M, N)).astype(np.float32) * 10)
+    got = oracle.gemm_fp8_fp4_nt(a, sfa, b, sfb, c)
+    for m in range(M):
+        for n in range(N):
+            tot = frac_bf16(int(c[m, n]))
+            for k in range(K):
+                e = int(ebytes[k // 128, n, (k % 128) // 32]) - 127
+                tot += (frac_e4m3(int(a[m, k])) * frac_f32(sfa[k // 128, m])
+                        * frac_e2m1(_nibble(b, n, k)) * Fraction(2) ** e)
+            assert int(got[m, n]) == frac_rne_bf16_bits(tot), (m, n)
+
+
+def test_fp8_fp4_quantiser_round_trip():
+    # every code decodes to a value the quantiser maps back to that code, and
+    # scales are powers of two with the block maximum within 6 * scale
+    x = np.random.default_rng(62).standard_normal((8, 256)).astype(np.float32)
+    packed, e = inputgen.quantize_fp4_rows(x)
+    vals = oracle.decode_e2m1_packed(packed) * np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+    amax = np.abs(x).reshape(8, 8, 32).max(axis=2)
+    s = np.ldexp(1.0, e.astype(np.int64) - 127)
+    assert np.all(amax <= 6 * s) and np.all(amax > 3 * s)
+    err = np.abs(vals - x)
+    assert np.all(err <= np.repeat(s, 32, axis=1) * 1.0 + 1e-12)     # half the widest E2M1 step (4 -> 6) times the scale
+    codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(8, 256)
+    assert np.array_equal(inputgen.encode_e2m1(oracle.E2M1_VALUES[codes]), np.where(codes == 8, 0, codes))
