@@ -4,12 +4,13 @@ One step is one library call over one batch of synthetic inputs already
 resident in HBM.  The headline workload is the dense decode shape
 M=64 N=2112 K=7168 (A ~ N(0,1), B ~ N(0,0.02), 1x128 / 128x128 power-of-two
 scales, bf16 C ~ N(0,0.1)); the other four workloads, the prefill problem
-with K-major operands (nn, tn, tt) and a K-grouped TN (MoE weight-gradient)
-problem are reported per shape in the same JSON line.  Inputs rotate over enough copies that successive steps
+with K-major operands (nn, tn, tt), a K-grouped TN (MoE weight-gradient)
+problem and the prefill problem with an FP4 B are reported per shape in the
+same JSON line.  Inputs rotate over enough copies that successive steps
 read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,2,3,4,5,6,7,8,9]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,10]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
 
@@ -53,6 +54,8 @@ SHAPES = {
     # K-grouped TN (MoE weight gradient): 8 experts, M=4096 x N=7168 per expert,
     # 8192 tokens split multinomially, fp32 D
     9: ("kgrouped_tn_8x4096x7168_tokens8192", "mfma"),
+    # FP8 x FP4: the prefill problem with B in E2M1, one E8M0 scale per 32 K values
+    10: ("dense_fp8xfp4_4096x7168x16384", "mfma"),
 }
 LAYOUT_OF = {6: "nn", 7: "tn", 8: "tt"}
 PROBLEM_OF = {6: 3, 7: 3, 8: 3}        # workload index whose generated problem a layout entry reuses
@@ -113,6 +116,9 @@ def algorithmic_bytes(p) -> int:
         used = np.unique(p.grouped_layout[p.grouped_layout >= 0])
         b = sum(p.b[g].nbytes + p.sfb[g].nbytes for g in used)
         return rows * p.K + rows * KB * 4 + rows * 4 + b + rows * p.N * 2
+    if isinstance(p, inputgen.DenseFP4):
+        cbytes = (p.M * p.N * 2) if p.c is not None else 0
+        return p.M * p.K + p.M * KB * 4 + p.b.nbytes + p.sfb.nbytes + cbytes + p.M * p.N * 2
     if isinstance(p, inputgen.KGrouped):
         tokens = int(p.counts.sum())
         return tokens * (p.M + p.N) + (tokens // 128 + p.G) * (p.M + p.N) * 4 + p.G * p.M * p.N * 4
@@ -132,6 +138,8 @@ class Workload:
         t0 = time.time()
         if idx == 9:
             self.p = p = inputgen.make_kgrouped(8, 4096, 7168, 8192, seed=0, name=SHAPES[idx][0])
+        elif idx == 10:
+            self.p = p = inputgen.make_dense_fp4(4096, 7168, 16384, 0, 1.0, 0.02, None, False, SHAPES[idx][0])
         else:
             self.p = p = inputgen.make_config(PROBLEM_OF.get(idx, idx) - 1, seed=0)
         self.name, self.bound = SHAPES[idx]
@@ -155,7 +163,7 @@ class Workload:
         for i in range(copies):
             s = dict(a=a if i == 0 else a.clone(), sfa=sfa if i == 0 else sfa.clone(),
                      b=b if i == 0 else b.clone(), sfb=sfb if i == 0 else sfb.clone())
-            if isinstance(p, inputgen.Dense):
+            if isinstance(p, (inputgen.Dense, inputgen.DenseFP4)):
                 s["c"] = up(p.c.view(np.int16)).view(torch.bfloat16) if p.c is not None else None
                 s["d"] = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
             elif isinstance(p, inputgen.Contiguous):
@@ -178,6 +186,8 @@ class Workload:
         dg = self.dg
         if self.kind == "Dense":
             getattr(dg, "dg_fp8_gemm_" + self.layout)(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
+        elif self.kind == "DenseFP4":
+            dg.dg_fp8_fp4_gemm_nt(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
         elif self.kind == "KGrouped":
             dg.dg_k_grouped_fp8_gemm_tn_contiguous(s["a"], s["sfa"], s["b"], s["sfb"], None, s["d"], self.p.ks)
         elif self.kind == "Contiguous":
@@ -246,7 +256,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9", help="comma-separated 1-based workload indices")
+    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")

@@ -84,6 +84,23 @@ int dg_fp8_gemm_tn(const void* a, const float* sfa, const void* b, const float* 
 int dg_fp8_gemm_tt(const void* a, const float* sfa, const void* b, const float* sfb,
                    const void* c, void* d, int M, int N, int K, void* stream);
 
+/* Dense FP8 x FP4 GEMM, NT layout (likun.im section 一: "fp8_fp4_gemm_nt";
+ * section 五: packed UE8M0 scale factors, four to an int; lqnn.cn: the FP8 x
+ * FP4 GEMM release):
+ *   D[m,n] = bf16_rne( C[m,n] + sum_kb sa[kb][m]
+ *            * sum_{k in block kb} A[m,k] * B[n,k] * 2^(e[n][k/32] - 127) )
+ *   a    uint8  [M][K]       e4m3 codes (16-byte aligned); sfa float [K/128][M] as in dg_fp8_gemm_nt
+ *   b    uint8  [N][K/2]     OCP E2M1 (FP4) codes, two per byte, element 2i in the
+ *                            low nibble, K contiguous (16-byte aligned)
+ *   sfb  int32  [K/128][N]   E8M0 scale exponents e (value 2^(e-127)), one byte per
+ *                            32 K values: byte j of sfb[kb][n] scales K values
+ *                            128*kb + 32*j .. +31 of row n (4-byte aligned)
+ *   c, d bf16   [M][N]       as in dg_fp8_gemm_nt
+ * K must be a multiple of 128.  Runs on the tile kernels (no split-K variant).
+ * Returns a dg_status. */
+int dg_fp8_fp4_gemm_nt(const void* a, const float* sfa, const void* b, const int32_t* sfb,
+                       const void* c, void* d, int M, int N, int K, void* stream);
+
 /* M-grouped GEMM, contiguous layout (likun.im section 二:
  * "m_grouped_..._gemm_nt_contiguous" taking grouped_layout): the rows of every
  * expert are concatenated along M.  grouped_layout is a device int32 array of

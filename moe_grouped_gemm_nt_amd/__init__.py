@@ -1,10 +1,12 @@
 """FP8 (e4m3) block-scaled GEMM (NT, and NN/TN/TT with K-major operands), with
-M-grouped MoE forms and the K-grouped TN form, for AMD MI355X (gfx950).  The kernels live in libdg.so behind the C ABI of
+M-grouped MoE forms, the K-grouped TN form and an FP8 x FP4 GEMM, for AMD
+MI355X (gfx950).  The kernels live in libdg.so behind the C ABI of
 include/dg.h; this package is its Python binding."""
 from ._lib import (  # noqa: F401
     DGError,
     EXPORTED,
     LIB_PATH,
+    dg_fp8_fp4_gemm_nt,
     dg_fp8_gemm_nn,
     dg_fp8_gemm_nt,
     dg_fp8_gemm_tn,

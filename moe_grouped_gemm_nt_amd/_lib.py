@@ -24,6 +24,7 @@ EXPORTED = [
     "dg_fp8_gemm_nn",
     "dg_fp8_gemm_tn",
     "dg_fp8_gemm_tt",
+    "dg_fp8_fp4_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
     "dg_k_grouped_fp8_gemm_tn_contiguous",
@@ -55,6 +56,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
             getattr(lib, name).argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp]
             getattr(lib, name).restype = ci
+        lib.dg_fp8_fp4_gemm_nt.argtypes = [vp, fp, vp, vp, vp, vp, ci, ci, ci, vp]
+        lib.dg_fp8_fp4_gemm_nt.restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, vp]
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
@@ -148,6 +151,17 @@ def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d, stream=None) -> None:
     K, M = a.shape
     N = b.shape[0]
     _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, M, N, K, stream)
+
+
+def dg_fp8_fp4_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """d[M][N] = bf16(c + a[M][K] . dequant(b)^T): b packed E2M1 [N][K/2], sfb int32 [K/128][N]
+    (four E8M0 exponents per int, one per 32 K values)."""
+    M, K = a.shape
+    N = b.shape[0]
+    _check("dg_fp8_fp4_gemm_nt", load().dg_fp8_fp4_gemm_nt(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
 
 
 def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:

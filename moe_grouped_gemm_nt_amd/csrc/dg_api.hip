@@ -108,8 +108,8 @@ int env_int(const char* name, int dflt) {
 }
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
-// kmajor: a dense call with a K-major operand (nn, tn, tt), which only the
-// 128x128, 128x256 and 256x256 tile kernels read
+// kmajor: a dense call with a K-major operand (nn, tn, tt) or an FP4 B, which
+// only the 128x128, 128x256 and 256x256 tile kernels read
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, bool kmajor) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const int KB = K / 128;
@@ -286,6 +286,27 @@ int dense_kmajor(const void* a, const float* sfa, const void* b, const float* sf
   return launch(dg::kDense, p, M, static_cast<hipStream_t>(stream));
 }
 }  // namespace
+
+extern "C" int dg_fp8_fp4_gemm_nt(const void* a, const float* sfa, const void* b, const int32_t* sfb,
+                                  const void* c, void* d, int M, int N, int K, void* stream) {
+  // b holds K/2 bytes per row; the common checks see the same pointers
+  int s = check_common(a, sfa, b, reinterpret_cast<const float*>(sfb), c, d, M, N, K);
+  if (s != DG_OK) return s;
+  if (M == 0 || N == 0) return DG_OK;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = reinterpret_cast<const float*>(sfb);   // copied as raw words by the kernel
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.G = 1;
+  p.ab_layout = 4;
+  return launch(dg::kDense, p, M, static_cast<hipStream_t>(stream));
+}
 
 extern "C" int dg_fp8_gemm_nn(const void* a, const float* sfa, const void* b, const float* sfb,
                               const void* c, void* d, int M, int N, int K, void* stream) {

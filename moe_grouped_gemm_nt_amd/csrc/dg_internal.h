@@ -31,7 +31,8 @@ struct Params {
   int tiles_n;             // ceil(N / BN)
   int splits;              // split-K factor (>= 1; decode kernel only)
   int kbs_per_split;       // K blocks per split (decode kernel only)
-  int ab_layout;           // dense: bit 0 = A stored [K][M], bit 1 = B stored [K][N] (0 = nt)
+  int ab_layout;           // dense: bit 0 = A stored [K][M], bit 1 = B stored [K][N] (0 = nt),
+                           // 4 = B packed FP4 (E2M1) with E8M0 scales, sfb int32 [K/128][N]
   float* d32;              // K-grouped: fp32 D [G][M][N]
   const float* c32;        // K-grouped: fp32 C [G][M][N] or nullptr
 };

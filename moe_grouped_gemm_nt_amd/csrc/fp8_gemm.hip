@@ -324,8 +324,9 @@ hipError_t launch_narrow(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Dense calls with K-major operands (nn, tn, tt) are compiled for the tiles
-// the chooser gives them: 128x128 (four waves, 4-slot ring), 128x256 and 256x256.
+// Dense calls with K-major operands (nn, tn, tt) and FP8 x FP4 calls are
+// compiled for the tiles the chooser gives them: 128x128 (four waves, 4-slot
+// ring), 128x256 and 256x256.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU, int LAYOUT>
 hipError_t launch_dense_layout(const Params& p, int grid, hipStream_t stream) {
   constexpr bool compiled = WG_PER_CU == 1 && ((BM == 128 && BN == 128 && NSLOT == 4) ||
@@ -347,6 +348,7 @@ hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
       case 1: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 1>(p, grid, stream);
       case 2: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 2>(p, grid, stream);
       case 3: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 3>(p, grid, stream);
+      case 4: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 4>(p, grid, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -79,6 +79,9 @@ __device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
+// FP4 rows are 64 bytes (four 16-byte chunks): chunk c of row r is stored at
+// c ^ swz4(r), so the 16 rows a fragment read touches cover all 16 bank groups.
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   __bf16 h = static_cast<__bf16>(x);   // v_cvt_pk_bf16_f32: round to nearest even
@@ -249,7 +252,8 @@ __device__ __forceinline__ v8i kmajor_frag(uint32_t addr) {
 // ============================================================================
 // CS: B scales per column per K block (the K-grouped form) instead of one per
 // 128x128 block: each wave loads 64 of them per block into its own area.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, bool CS = false>
+// B4: B holds packed FP4 codes, 64 bytes per row per K block.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, bool CS = false, bool B4 = false>
 struct Shape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
@@ -258,7 +262,8 @@ struct Shape {
   static constexpr int SM = WTM / 16;           // 16-row strips per wave
   static constexpr int SN = WTN / 16;           // 16-col strips per wave
   static constexpr int A_BYTES = BM * KBLK;     // one slot of each region
-  static constexpr int B_BYTES = BN * KBLK;
+  static constexpr int B_ROW = B4 ? KBLK / 2 : KBLK;   // bytes of one B row per K block
+  static constexpr int B_BYTES = BN * B_ROW;
   static constexpr int RS = BM / NWAVES;        // row scales loaded per wave
   // with 64 row scales per wave the B scale needs a load of its own
   static constexpr bool SB_SEP = RS >= 64;
@@ -277,13 +282,13 @@ struct Shape {
   static constexpr int SC_REGION = NSLOT * (A_BYTES + B_BYTES + S_BYTES);
   static constexpr int LDS_BYTES = NSLOT * (A_BYTES + B_BYTES + S_BYTES + SC_BYTES);
   static constexpr int A_INSTR = BM / 8 / NWAVES;     // 1 KB (8 rows) per wave instruction
-  static constexpr int B_INSTR = BN / 8 / NWAVES;
+  static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
   static constexpr int LPS = A_INSTR + B_INSTR + 1 + SB_SEP + CS;   // loads per wave per K block
   static_assert(!CS || (BN % 64 == 0 && BN / 64 <= NWAVES), "column scales: one 64-column load per wave");
   static_assert(NWAVES == 4 || NWAVES == 8, "four or eight waves per workgroup");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must sit in one 128-wide B scale block");
-  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "every wave issues the same number of loads");
+  static_assert(BM % (8 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "every wave issues the same number of loads");
   static_assert(RS % 4 == 0 && RS <= 64, "row scales fit one 64-lane load per wave");
   static_assert((NSLOT - 1) * LPS < 64, "outstanding loads must fit the 6-bit vmcnt");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
@@ -326,9 +331,11 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int MODE, int WG_
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64, WG_PER_CU)
 fp8_gemm_nt_kernel(PT p) {
   constexpr bool KG = MODE == kKGrouped;
-  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT, KG>;
+  constexpr bool B4 = (LAYOUT & 4) != 0;    // FP8 x FP4: B packed E2M1, E8M0 scales per row per 32 K
+  using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT, KG || B4, B4>;
   constexpr bool TA = (LAYOUT & 1) != 0, TB = (LAYOUT & 2) != 0;
-  static_assert(LAYOUT == 0 || MODE == kDense || (KG && LAYOUT == 3),
+  static_assert(!B4 || (LAYOUT == 4 && MODE == kDense && !E8M0), "FP8 x FP4: dense NT, fp32 promotion");
+  static_assert(LAYOUT == 0 || LAYOUT == 4 || MODE == kDense || (KG && LAYOUT == 3),
                 "K-major operands are supported by the dense and K-grouped forms");
   static_assert(!KG || (LAYOUT == 3 && !E8M0), "the K-grouped form reads K-major operands with fp32 promotion");
   static_assert((!TA || S::WTM % 32 == 0) && (!TB || S::WTN % 32 == 0), "K-major strips pair up in 32-row steps");
@@ -369,10 +376,19 @@ fp8_gemm_nt_kernel(PT p) {
   uint32_t offA0[2], offB0[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    // The fp8 operand of the 16x16x128 MFMA holds, in lane group g = l/16,
+    // K bytes 16g..16g+15 in its low four dwords and 64+16g..64+16g+15 in the
+    // high four (measured against the FP4 operand, whose lane group s holds K
+    // 32s..32s+31).  Two fp8 operands only need the same K order, so the fp8 x
+    // fp8 kernels read chunks 2g and 2g+1; against an FP4 B, A reads chunks g
+    // and 4+g.
     offA0[h] = smem_base + (TA ? kmajor_frag_base<BM>(wrow0, lane, h)
-                               : (wrow0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4));
+                               : (wrow0 + r16) * KBLK + (((B4 ? 4 * h + g16 : 2 * g16 + h) ^ swz(r16)) << 4));
+    // FP4 B: a 64-byte row per K block, the lane's 16 bytes (32 codes) at chunk
+    // g16 of its column, chunks XOR-swizzled by (row / 4) % 4
     offB0[h] = smem_base + S::B_REGION + (TB ? kmajor_frag_base<BN>(wcol0, lane, h)
-                                             : (wcol0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4));
+                                          : B4 ? (wcol0 + r16) * S::B_ROW + ((g16 ^ swz4(r16)) << 4)
+                                               : (wcol0 + r16) * KBLK + (((2 * g16 + h) ^ swz(r16)) << 4));
   }
   // row scales of the lane's four result rows in strip 0 (strip i adds strip_scale_off(i))
   const uint32_t offS0 = smem_base + S::S_REGION +
@@ -507,7 +523,7 @@ fp8_gemm_nt_kernel(PT p) {
       D32 = p.d32 + (size_t)group * a_rows * p.N;
       if (p.c32) C32 = p.c32 + (size_t)group * a_rows * p.N;
     }
-    int nb = KG ? 0 : (n0 + wcol0) / 128;
+    int nb = (KG || B4) ? 0 : (n0 + wcol0) / 128;
     nb = nb < NB ? nb : NB - 1;
 
     // ---- load addresses -------------------------------------------------------
@@ -520,9 +536,9 @@ fp8_gemm_nt_kernel(PT p) {
     // ones re-read the last valid 16 columns (rows_lim and N are multiples of
     // 16 for such operands), whose results are never stored.
     const uint8_t* a_tile = TA ? A + m0 : A + (size_t)m0 * p.K;
-    const uint8_t* b_tile = TB ? B + n0 : B + (size_t)n0 * p.K;
+    const uint8_t* b_tile = TB ? B + n0 : B + (size_t)n0 * (p.K / KBLK) * S::B_ROW;
     const size_t a_kstep = TA ? (size_t)KBLK * a_rows : KBLK;
-    const size_t b_kstep = TB ? (size_t)KBLK * p.N : KBLK;
+    const size_t b_kstep = TB ? (size_t)KBLK * p.N : S::B_ROW;
     uint32_t a_off[S::A_INSTR], b_off[S::B_INSTR];
 #pragma unroll
     for (int j = 0; j < S::A_INSTR; ++j) {
@@ -540,7 +556,13 @@ fp8_gemm_nt_kernel(PT p) {
     }
 #pragma unroll
     for (int j = 0; j < S::B_INSTR; ++j) {
-      if constexpr (TB) {
+      if constexpr (B4) {
+        // FP4 B: instruction j covers tile rows 16*(wave + NWAVES*j) .. +15, four
+        // 16-byte chunks each; lane l loads row .. + l/4, logical chunk (l%4) ^ swz4
+        const int r = (wave + S::NWAVES * j) * 16 + (lane >> 2);
+        const int gn = min(n0 + r, p.N - 1);
+        b_off[j] = (uint32_t)((gn - n0) * (p.K / 2)) + (((lane & 3) ^ swz4(r)) << 4);
+      } else if constexpr (TB) {
         int kr, c;
         kmajor_slot<BN>(64 * (wave + S::NWAVES * j) + lane, kr, c);
         b_off[j] = (uint32_t)(kr * p.N + (min(n0 + 16 * c, p.N - 16) - n0));
@@ -601,7 +623,7 @@ fp8_gemm_nt_kernel(PT p) {
     auto compute = [&](auto u_const, int next, int next_u, float live) {
       constexpr int u = decltype(u_const)::value;
       // the block's B scale (K-grouped: 1, the per-column scales enter below)
-      const float sb = KG ? live : lds_f32(offSB + u * S::S_BYTES) * live;
+      const float sb = (KG || B4) ? live : lds_f32(offSB + u * S::S_BYTES) * live;
       auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) {
         const v4i lo = lds_v4i(lo_addr), hi = lds_v4i(hi_addr);
         return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -612,6 +634,10 @@ fp8_gemm_nt_kernel(PT p) {
         else return frag(offA0[0] + i * 2048 + u * S::A_BYTES, offA0[1] + i * 2048 + u * S::A_BYTES);
       };
       auto fragB = [&](int j) {
+        if constexpr (B4) {
+          const v4i q = lds_v4i(offB0[0] + j * 16 * S::B_ROW + u * S::B_BYTES);
+          return (v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};   // FP4 operands use the low four dwords
+        }
         if constexpr (TB) return kmajor_frag<BN>(offB0[j & 1] + j * 128 + u * S::B_BYTES);
         else return frag(offB0[0] + j * 2048 + u * S::B_BYTES, offB0[1] + j * 2048 + u * S::B_BYTES);
       };
@@ -653,8 +679,12 @@ fp8_gemm_nt_kernel(PT p) {
       for (int j = 0; j < S::SN; ++j)
         bf[j] = fragB(j);
       float sbc[S::SN];               // K-grouped: the lane's column scale in each column strip
+      int esb[S::SN];                 // FP4 B: E8M0 scale of the lane's column and 32-K slice
 #pragma unroll
-      for (int j = 0; j < S::SN; ++j) sbc[j] = KG ? lds_f32(offSC + j * 64 + u * S::SC_BYTES) : 1.f;
+      for (int j = 0; j < S::SN; ++j) {
+        sbc[j] = KG ? lds_f32(offSC + j * 64 + u * S::SC_BYTES) : 1.f;
+        esb[j] = B4 ? (int)((__float_as_uint(lds_f32(offSC + j * 64 + u * S::SC_BYTES)) >> (8 * g16)) & 0xFF) : 0;
+      }
       // A strips are read one strip ahead of their MFMAs, which bounds the live
       // A fragments to two
       auto load_strip = [&](int i) {
@@ -673,8 +703,12 @@ fp8_gemm_nt_kernel(PT p) {
             load_strip(t / S::SN + 1);
           }
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
-          part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
-                                                                         0, 0, 0, 0, 0, 0);
+          if constexpr (B4)   // B format FP4 (E2M1), its E8M0 scale per lane; A unscaled (2^0)
+            part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
+                                                                           0, 4, 0, 127, 0, esb[t % S::SN]);
+          else
+            part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / S::SN], bf[t % S::SN], zero,
+                                                                           0, 0, 0, 0, 0, 0);
           // spread the LPS loads of the next block over the first MFMAs
           if (t % STRIDE == 0 && t / STRIDE < S::LPS) issue_one(t / STRIDE, next, next_u);
         }

@@ -1,0 +1,70 @@
+"""Parity of the FP8 x FP4 call (B packed E2M1 with per-32 E8M0 scales) with
+the oracle, through the C ABI.  Exact-regime inputs must match bit for bit;
+random inputs meet the NT call's bf16 tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import oracle
+from tests.gpu_util import bf16_bits_dev, bits_host, check_tolerance, dev, sentinel_like
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_grouped_gemm_nt_amd as m
+    m.dg_init()
+    return m
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def run_fp4(dg, p):
+    d = sentinel_like((p.M, p.N))
+    c = bf16_bits_dev(p.c) if p.c is not None else None
+    dg.dg_fp8_fp4_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), c, d)
+    torch.cuda.synchronize()
+    return bits_host(d)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (300, 400, 512), (17, 48, 256), (64, 2112, 7168), (528, 272, 1024)])
+def test_fp4_exact(dg, M, N, K):
+    log(f"case: fp8 x fp4 exact {M}x{N}x{K}")
+    p = inputgen.exact_dense_fp4(M, N, K, seed=M + N)
+    assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("cfg", ["0", "6", "11"])
+def test_fp4_every_tile_config_exact(dg, monkeypatch, cfg):
+    log(f"case: fp8 x fp4 exact, forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = inputgen.exact_dense_fp4(400, 592, 640, seed=3)
+    assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("pow2", [True, False])
+def test_fp4_random_tolerance(dg, pow2):
+    log(f"case: fp8 x fp4 random, A pow2 scales {pow2}")
+    p = inputgen.make_dense_fp4(256, 384, 2048, 9, 1.0, 0.02, 0.1, pow2)
+    check_tolerance(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c), "fp4")
+
+
+def test_fp4_wide_scale_range(dg):
+    # E8M0 exponents spread over 2^-20 .. 2^20 on the first 32-K slice of every
+    # block: checks that each slice takes its own scale byte (sums of very
+    # different magnitudes round in fp32, so the bound is the bf16 tolerance)
+    log("case: fp8 x fp4 with scale exponents spread over 2^-20 .. 2^20")
+    p = inputgen.exact_dense_fp4(64, 128, 256, seed=4, with_c=False)
+    q = p.sfb.view(np.uint32).copy()
+    rng = np.random.default_rng(5)
+    shift = rng.integers(-20, 21, size=q.shape).astype(np.int64)
+    b0 = ((q & 0xFF).astype(np.int64) + shift).clip(1, 254).astype(np.uint32)
+    q = (q & ~np.uint32(0xFF)) | b0
+    p.sfb = q.view(np.int32)
+    check_tolerance(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c), "fp4 scales")
