@@ -130,6 +130,9 @@ def algorithmic_bytes(p) -> int:
     raise TypeError(p)
 
 
+_PROBLEMS = {}      # generated problems by workload index, shared by the entries that reuse one
+
+
 class Workload:
     """Device copies of one generated problem plus the launch closure."""
 
@@ -141,7 +144,10 @@ class Workload:
         elif idx == 10:
             self.p = p = inputgen.make_dense_fp4(4096, 7168, 16384, 0, 1.0, 0.02, None, False, SHAPES[idx][0])
         else:
-            self.p = p = inputgen.make_config(PROBLEM_OF.get(idx, idx) - 1, seed=0)
+            src = PROBLEM_OF.get(idx, idx)
+            if src not in _PROBLEMS:          # the layout entries reuse the prefill problem
+                _PROBLEMS[src] = inputgen.make_config(src - 1, seed=0)
+            self.p = p = _PROBLEMS[src]
         self.name, self.bound = SHAPES[idx]
         self.layout = LAYOUT_OF.get(idx, "nt")
         self.flops = p.flops
