@@ -131,6 +131,21 @@ int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void*
                                     int K, int num_groups, const int32_t* masked_m,
                                     int expected_m, void* stream);
 
+/* M-grouped FP8 x FP4 GEMMs (likun.im section 二: "m_grouped_fp8_fp4_gemm_nt_contiguous"
+ * and "..._masked"): as dg_m_grouped_fp8_gemm_nt_contiguous / _masked with the
+ * FP4 B of dg_fp8_fp4_gemm_nt per group: b uint8 [G][N][K/2] (packed E2M1),
+ * sfb int32 [G][K/128][N] (four E8M0 exponents per int).  A, sfa, C, D,
+ * grouped_layout, masked_m and expected_m exactly as in the FP8 forms.
+ * Returns a dg_status. */
+int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
+                                            const int32_t* sfb, const void* c, void* d, int M, int N,
+                                            int K, int num_groups, const int32_t* grouped_layout,
+                                            void* stream);
+int dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* sfa, const void* b,
+                                        const int32_t* sfb, const void* c, void* d, int max_m, int N,
+                                        int K, int num_groups, const int32_t* masked_m,
+                                        int expected_m, void* stream);
+
 /* K-grouped GEMM, TN layout, for MoE weight gradients (likun.im section 一:
  * "k_grouped_fp8_gemm_tn", grouped along K for the MoE backward pass; section
  * 二: the call takes the per-group K sizes ks and the (1, 1, 128) scale

@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     dg_fp8_gemm_tt,
     dg_init,
     dg_k_grouped_fp8_gemm_tn_contiguous,
+    dg_m_grouped_fp8_fp4_gemm_nt_contiguous,
+    dg_m_grouped_fp8_fp4_gemm_nt_masked,
     dg_m_grouped_fp8_gemm_nt_contiguous,
     dg_m_grouped_fp8_gemm_nt_masked,
     dg_version,

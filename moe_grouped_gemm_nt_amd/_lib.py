@@ -27,6 +27,8 @@ EXPORTED = [
     "dg_fp8_fp4_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
+    "dg_m_grouped_fp8_fp4_gemm_nt_contiguous",
+    "dg_m_grouped_fp8_fp4_gemm_nt_masked",
     "dg_k_grouped_fp8_gemm_tn_contiguous",
     "dg_init",
     "dg_last_error",
@@ -62,6 +64,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ci
         lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
         lib.dg_m_grouped_fp8_gemm_nt_masked.restype = ci
+        lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous.argtypes = [vp, fp, vp, vp, vp, vp, ci, ci, ci, ci, i32p, vp]
+        lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous.restype = ci
+        lib.dg_m_grouped_fp8_fp4_gemm_nt_masked.argtypes = [vp, fp, vp, vp, vp, vp, ci, ci, ci, ci, i32p, ci, vp]
+        lib.dg_m_grouped_fp8_fp4_gemm_nt_masked.restype = ci
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp, vp]
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = ci
         lib.dg_init.argtypes = []
@@ -197,3 +203,26 @@ def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, c, d, ks, stream=None) -
         _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
         _ptr(c, "c", (torch.float32,), True), _ptr(d, "d", (torch.float32,)), M, N, len(ks),
         ctypes.cast(ks_host, ctypes.c_void_p), _stream(stream)))
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:
+    """Contiguous M-grouped FP8 x FP4 form: a [M][K], b packed [G][N][K/2], sfb int32 [G][K/128][N]."""
+    M, K = a.shape
+    G, N, _ = b.shape
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_contiguous", load().dg_m_grouped_fp8_fp4_gemm_nt_contiguous(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, G,
+        _ptr(grouped_layout, "grouped_layout", (torch.int32,)), _stream(stream)))
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, c, d, masked_m, expected_m, stream=None) -> None:
+    """Masked M-grouped FP8 x FP4 form: a [G][max_m][K], b packed [G][N][K/2], sfb int32 [G][K/128][N]."""
+    G, max_m, K = a.shape
+    N = b.shape[1]
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_masked", load().dg_m_grouped_fp8_fp4_gemm_nt_masked(
+        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
+        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
+        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), max_m, N, K, G,
+        _ptr(masked_m, "masked_m", (torch.int32,)), int(expected_m), _stream(stream)))
+

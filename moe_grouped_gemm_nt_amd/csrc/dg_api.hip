@@ -382,10 +382,12 @@ extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* s
   return DG_OK;
 }
 
-extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
-                                                   const float* sfb, const void* c, void* d, int M,
-                                                   int N, int K, int num_groups,
-                                                   const int32_t* grouped_layout, void* stream) {
+namespace {
+// M-grouped calls; ab_layout 0 = FP8 B [G][N][K] with fp32 128x128 scales,
+// 4 = FP4 B [G][N][K/2] with packed E8M0 scales [G][K/128][N].
+int grouped_contiguous(const void* a, const float* sfa, const void* b, const float* sfb, const void* c, void* d,
+                       int M, int N, int K, int num_groups, const int32_t* grouped_layout, int ab_layout,
+                       void* stream) {
   int s = check_common(a, sfa, b, sfb, c, d, M, N, K);
   if (s != DG_OK) return s;
   if (num_groups < 1) return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be at least 1", num_groups);
@@ -404,13 +406,13 @@ extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* s
   p.N = N;
   p.K = K;
   p.G = num_groups;
+  p.ab_layout = ab_layout;
   return launch(dg::kContiguous, p, M, static_cast<hipStream_t>(stream));
 }
 
-extern "C" int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b,
-                                               const float* sfb, const void* c, void* d, int max_m,
-                                               int N, int K, int num_groups, const int32_t* masked_m,
-                                               int expected_m, void* stream) {
+int grouped_masked(const void* a, const float* sfa, const void* b, const float* sfb, const void* c, void* d,
+                   int max_m, int N, int K, int num_groups, const int32_t* masked_m, int expected_m, int ab_layout,
+                   void* stream) {
   int s = check_common(a, sfa, b, sfb, c, d, max_m, N, K);
   if (s != DG_OK) return s;
   if (num_groups < 1) return fail(DG_ERR_INVALID_ARG, "num_groups=%d must be at least 1", num_groups);
@@ -431,7 +433,39 @@ extern "C" int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, 
   p.N = N;
   p.K = K;
   p.G = num_groups;
+  p.ab_layout = ab_layout;
   return launch(dg::kMasked, p, expected_m > 0 ? expected_m : max_m, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" int dg_m_grouped_fp8_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
+                                                   const float* sfb, const void* c, void* d, int M,
+                                                   int N, int K, int num_groups,
+                                                   const int32_t* grouped_layout, void* stream) {
+  return grouped_contiguous(a, sfa, b, sfb, c, d, M, N, K, num_groups, grouped_layout, 0, stream);
+}
+
+extern "C" int dg_m_grouped_fp8_gemm_nt_masked(const void* a, const float* sfa, const void* b,
+                                               const float* sfb, const void* c, void* d, int max_m,
+                                               int N, int K, int num_groups, const int32_t* masked_m,
+                                               int expected_m, void* stream) {
+  return grouped_masked(a, sfa, b, sfb, c, d, max_m, N, K, num_groups, masked_m, expected_m, 0, stream);
+}
+
+extern "C" int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const void* a, const float* sfa, const void* b,
+                                                       const int32_t* sfb, const void* c, void* d, int M,
+                                                       int N, int K, int num_groups,
+                                                       const int32_t* grouped_layout, void* stream) {
+  return grouped_contiguous(a, sfa, b, reinterpret_cast<const float*>(sfb), c, d, M, N, K, num_groups,
+                            grouped_layout, 4, stream);
+}
+
+extern "C" int dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* sfa, const void* b,
+                                                   const int32_t* sfb, const void* c, void* d, int max_m,
+                                                   int N, int K, int num_groups, const int32_t* masked_m,
+                                                   int expected_m, void* stream) {
+  return grouped_masked(a, sfa, b, reinterpret_cast<const float*>(sfb), c, d, max_m, N, K, num_groups, masked_m,
+                        expected_m, 4, stream);
 }
 
 extern "C" int dg_init(void) {

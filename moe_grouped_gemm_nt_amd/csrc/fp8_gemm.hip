@@ -340,9 +340,31 @@ hipError_t launch_dense_layout(const Params& p, int grid, hipStream_t stream) {
   }
 }
 
+// M-grouped FP8 x FP4 calls, on the same tiles.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU, int MODE>
+hipError_t launch_grouped_fp4(const Params& p, int grid, hipStream_t stream) {
+  constexpr bool compiled = WG_PER_CU == 1 && ((BM == 128 && BN == 128 && NSLOT == 4) ||
+                                               (BM == 128 && BN == 256) || (BM == 256 && BN == 256));
+  if constexpr (compiled) {
+    hipLaunchKernelGGL((fp8_gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, NSLOT, MODE, WG_PER_CU, false, 4>),
+                       dim3(grid), dim3(WAVES_M * WAVES_N * 64), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSLOT, int WG_PER_CU = 1>
 hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
   constexpr int threads = WAVES_M * WAVES_N * 64;
+  if (mode != kDense && p.ab_layout != 0) {
+    if (p.ab_layout != 4) return hipErrorInvalidValue;
+    if (mode == kContiguous)
+      return launch_grouped_fp4<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, kContiguous>(p, grid, stream);
+    if (mode == kMasked)
+      return launch_grouped_fp4<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, kMasked>(p, grid, stream);
+    return hipErrorInvalidValue;
+  }
   if (mode == kDense && p.ab_layout != 0) {
     switch (p.ab_layout) {
       case 1: return launch_dense_layout<BM, BN, WAVES_M, WAVES_N, NSLOT, WG_PER_CU, 1>(p, grid, stream);

@@ -334,7 +334,7 @@ fp8_gemm_nt_kernel(PT p) {
   constexpr bool B4 = (LAYOUT & 4) != 0;    // FP8 x FP4: B packed E2M1, E8M0 scales per row per 32 K
   using S = Shape<BM, BN, WAVES_M, WAVES_N, NSLOT, KG || B4, B4>;
   constexpr bool TA = (LAYOUT & 1) != 0, TB = (LAYOUT & 2) != 0;
-  static_assert(!B4 || (LAYOUT == 4 && MODE == kDense && !E8M0), "FP8 x FP4: dense NT, fp32 promotion");
+  static_assert(!B4 || (LAYOUT == 4 && !KG && !E8M0), "FP8 x FP4: NT storage (dense or M-grouped), fp32 promotion");
   static_assert(LAYOUT == 0 || LAYOUT == 4 || MODE == kDense || (KG && LAYOUT == 3),
                 "K-major operands are supported by the dense and K-grouped forms");
   static_assert(!KG || (LAYOUT == 3 && !E8M0), "the K-grouped form reads K-major operands with fp32 promotion");
@@ -509,8 +509,13 @@ fp8_gemm_nt_kernel(PT p) {
       if (C) C += (size_t)group * p.rows * p.N;
     }
     if constexpr (MODE == kContiguous || MODE == kMasked) {
-      B += (size_t)group * p.N * p.K;
-      SB += (size_t)group * NB * KB;
+      if constexpr (B4) {                 // packed FP4 rows and int32 [K/128][N] E8M0 scales per group
+        B += (size_t)group * p.N * (p.K / 2);
+        SB += (size_t)group * KB * p.N;
+      } else {
+        B += (size_t)group * p.N * p.K;
+        SB += (size_t)group * NB * KB;
+      }
     }
     float* D32 = nullptr;
     const float* C32 = nullptr;

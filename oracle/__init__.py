@@ -26,4 +26,6 @@ from .fp8_fp4 import (  # noqa: F401
     decode_e2m1_packed,
     gemm_fp8_fp4_nt_acc,
     gemm_fp8_fp4_nt,
+    m_grouped_fp8_fp4_contiguous,
+    m_grouped_fp8_fp4_masked,
 )

@@ -87,3 +87,46 @@ def gemm_fp8_fp4_nt_acc(a, sfa, b, sfb, c=None, rows=None, cols=None) -> np.ndar
 def gemm_fp8_fp4_nt(a, sfa, b, sfb, c=None, rows=None, cols=None) -> np.ndarray:
     """bf16 bits of D (see the module docstring)."""
     return round_f64_to_bf16_bits(gemm_fp8_fp4_nt_acc(a, sfa, b, sfb, c, rows, cols))
+
+
+def m_grouped_fp8_fp4_contiguous(a, sfa, b, sfb, grouped_layout, c=None, rows=None, cols=None):
+    """M-grouped contiguous FP8 x FP4 form ([likun] section 二 lists
+    "m_grouped_fp8_fp4_gemm_nt_contiguous" with grouped_layout): row m is the
+    dense FP8 x FP4 product of A[m] with expert grouped_layout[m]'s B (packed
+    [G][N][K/2]) and scales (sfb [G][K/128][N]); rows whose id lies outside
+    [0, G) are not part of the result.  Returns (bits [R][Cn], written [R])."""
+    M, K = a.shape
+    G, N, _ = b.shape
+    layout = np.asarray(grouped_layout)
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    cols = np.arange(N) if cols is None else np.asarray(cols)
+    out = np.zeros((len(rows), len(cols)), dtype=np.uint16)
+    ids = layout[rows]
+    written = (ids >= 0) & (ids < G)
+    for g in np.unique(ids[written]):
+        sel = np.nonzero(ids == g)[0]
+        rsel = rows[sel]
+        cg = None if c is None else np.asarray(c)[rsel]
+        out[sel] = gemm_fp8_fp4_nt(a[rsel], sfa[:, rsel], b[g], sfb[g], cg, None, cols)
+    return out, written
+
+
+def m_grouped_fp8_fp4_masked(a, sfa, b, sfb, masked_m, c=None, groups=None, cols=None):
+    """M-grouped masked FP8 x FP4 form ([likun] section 二,
+    "m_grouped_fp8_fp4_gemm_nt_masked"): group g's first min(masked_m[g], max_m)
+    rows are the dense FP8 x FP4 product with B[g]; later rows are not part of
+    the result.  Returns (bits [G'][max_m][Cn], written [G'][max_m])."""
+    G, max_m, K = a.shape
+    N = b.shape[1]
+    groups = np.arange(G) if groups is None else np.asarray(groups)
+    cols = np.arange(N) if cols is None else np.asarray(cols)
+    out = np.zeros((len(groups), max_m, len(cols)), dtype=np.uint16)
+    written = np.zeros((len(groups), max_m), dtype=bool)
+    for i, g in enumerate(groups):
+        m = int(min(max(int(masked_m[g]), 0), max_m))
+        if m == 0:
+            continue
+        cg = None if c is None else np.asarray(c)[g][:m]
+        out[i, :m] = gemm_fp8_fp4_nt(a[g][:m], sfa[g][:, :m], b[g], sfb[g], cg, None, cols)
+        written[i, :m] = True
+    return out, written

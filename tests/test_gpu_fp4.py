@@ -68,3 +68,53 @@ def test_fp4_wide_scale_range(dg):
     q = (q & ~np.uint32(0xFF)) | b0
     p.sfb = q.view(np.int32)
     check_tolerance(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c), "fp4 scales")
+
+
+def _fp4_experts(G, N, K, seed):
+    ps = [inputgen.exact_dense_fp4(1, N, K, seed=seed + g, with_c=False) for g in range(G)]
+    return np.stack([q.b for q in ps]), np.stack([q.sfb for q in ps])
+
+
+@pytest.mark.parametrize("cfg", [None, "0", "6", "11"])
+def test_fp4_contiguous_exact(dg, monkeypatch, cfg):
+    log(f"case: fp8 x fp4 contiguous exact, config {cfg}")
+    if cfg is not None:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    G, N, K = 3, 272, 512
+    counts = [200, 5, 300]
+    segs = [((c + 127) // 128) * 128 for c in counts]
+    layout = np.full(sum(segs), -1, dtype=np.int32)
+    off = 0
+    for g, (cnt, sg) in enumerate(zip(counts, segs)):
+        layout[off:off + cnt] = g
+        off += sg
+    base = inputgen.exact_dense_fp4(len(layout), N, K, seed=21)
+    b, sfb = _fp4_experts(G, N, K, 30)
+    d = sentinel_like((len(layout), N))
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(dev(base.a), dev(base.sfa), dev(b), dev(sfb),
+                                               bf16_bits_dev(base.c), d, dev(layout))
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_fp8_fp4_contiguous(base.a, base.sfa, b, sfb, layout, base.c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == 0xDEAD)
+
+
+@pytest.mark.parametrize("cfg", [None, "0", "6", "11"])
+def test_fp4_masked_exact(dg, monkeypatch, cfg):
+    log(f"case: fp8 x fp4 masked exact, config {cfg}")
+    if cfg is not None:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    G, max_m, N, K = 4, 288, 256, 384
+    base = inputgen.exact_dense_fp4(G * max_m, N, K, seed=22, with_c=False)
+    a = base.a.reshape(G, max_m, K)
+    sfa = np.ascontiguousarray(base.sfa.reshape(K // 128, G, max_m).transpose(1, 0, 2))
+    b, sfb = _fp4_experts(G, N, K, 40)
+    masked_m = np.array([288, 0, 1, 140], dtype=np.int32)
+    d = sentinel_like((G, max_m, N))
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(dev(a), dev(sfa), dev(b), dev(sfb), None, d, dev(masked_m), 128)
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_fp8_fp4_masked(a, sfa, b, sfb, masked_m)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == 0xDEAD)

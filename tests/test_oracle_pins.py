@@ -544,3 +544,40 @@ def test_fp8_fp4_quantiser_round_trip():
     assert np.all(err <= np.repeat(s, 32, axis=1) * 1.0 + 1e-12)     # half the widest E2M1 step (4 -> 6) times the scale
     codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(8, 256)
     assert np.array_equal(inputgen.encode_e2m1(oracle.E2M1_VALUES[codes]), np.where(codes == 8, 0, codes))
+
+
+def test_fp8_fp4_grouped_forms_reduce_to_brute_force_rows():
+    # contiguous: every valid row equals the exact-rational result with its
+    # expert's B; masked: the first masked_m rows of each group likewise
+    rng = np.random.default_rng(63)
+    G, N, K = 3, 4, 128
+    layout = np.array([0, 2, 2, -1, 1, 5], dtype=np.int32)
+    M = len(layout)
+    a = _random_codes(rng, (M, K))
+    b = rng.integers(0, 256, size=(G, N, K // 2)).astype(np.uint8)
+    sfa = rng.uniform(0.1, 2.0, size=(K // 128, M)).astype(np.float32)
+    eb = rng.integers(124, 131, size=(G, K // 128, N, 4)).astype(np.uint32)
+    sfb = (eb[..., 0] | (eb[..., 1] << 8) | (eb[..., 2] << 16) | (eb[..., 3] << 24)).view(np.int32)
+    got, written = oracle.m_grouped_fp8_fp4_contiguous(a, sfa, b, sfb, layout)
+    assert written.tolist() == [True, True, True, False, True, False]
+    for m in range(M):
+        g = int(layout[m])
+        if not 0 <= g < G:
+            continue
+        for n in range(N):
+            tot = Fraction(0)
+            for k in range(K):
+                tot += (frac_e4m3(int(a[m, k])) * frac_f32(sfa[k // 128, m]) * frac_e2m1(_nibble(b[g], n, k))
+                        * Fraction(2) ** (int(eb[g, k // 128, n, (k % 128) // 32]) - 127))
+            assert int(got[m, n]) == frac_rne_bf16_bits(tot), (m, n)
+    masked_m = np.array([2, 0, 7], dtype=np.int32)
+    am = a[:6].reshape(3, 2, K).repeat(2, axis=1)[:, :3]            # [G][max_m=3][K]
+    sfam = np.ascontiguousarray(np.repeat(sfa[:, None, :3], G, axis=1).transpose(1, 0, 2))   # [G][KB][3]
+    gm, wm = oracle.m_grouped_fp8_fp4_masked(am, sfam, b, sfb, masked_m)
+    assert wm.tolist() == [[True, True, False], [False, False, False], [True, True, True]]
+    for g in range(G):
+        m = min(int(masked_m[g]), 3)
+        if m:
+            ref = oracle.gemm_fp8_fp4_nt(am[g][:m], sfam[g][:, :m], b[g], sfb[g])
+            assert np.array_equal(gm[g, :m], ref)
+
