@@ -18,6 +18,7 @@
 //     loads, not the promotion, so they are not the default.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -181,7 +182,8 @@ int plan(int mode, int cfg, dg::Params& p, const DeviceState* st, bool gated) {
   p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
   p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
   long long items;
-  const long long resident = (long long)st->num_cus * (ci.bm * ci.bn <= 128 * 128 ? 2 : 1);
+  // one workgroup per CU, except the two-workgroup 128x128 configuration
+  const long long resident = (long long)st->num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
   if (mode == dg::kMasked) {
     items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
     if (items > resident) items = resident;
@@ -196,6 +198,47 @@ int plan(int mode, int cfg, dg::Params& p, const DeviceState* st, bool gated) {
   return (int)(((items + 7) / 8) * 8);
 }
 
+// Split tail: with a persistent grid of one workgroup per resident slot, the
+// items of an XCD that do not fill a last round are split over K so that the
+// round's workgroups all take a part (dense and 128-row contiguous calls on
+// tiles up to 128x256; the tile kernel writes fp32 partials that
+// splitk_tile_reduce_kernel sums).  Returns the grid (0 = no split tail) and
+// sets p.sk_splits / p.sk_tail.
+int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
+  const dg::ConfigInfo& ci = dg::config_info(cfg);
+  p.sk_splits = 1;
+  p.sk_tail = 0;
+  if (mode == dg::kMasked || p.ab_layout != 0 || ci.bm * ci.bn > 128 * 256) return 0;
+  if (mode == dg::kContiguous && ci.bm > 128) return 0;
+  if (cfg == dg::kCfgDecode || cfg == dg::kCfgNarrow || cfg == dg::kCfgE8_128x256 || cfg == dg::kCfgWs_128x256 ||
+      cfg == dg::kCfgE8_256x256)
+    return 0;
+  const int KB = p.K / 128;
+  const int resident = st->num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
+  const int grid = resident / 8 * 8;
+  const int slots = grid / 8;
+  const long long total = (long long)p.tiles_m * p.tiles_n;
+  const long long per_xcd = (total + 7) / 8;
+  int tail = 0;
+  for (int x = 0; x < 8; ++x) {
+    long long n_x = total - x * per_xcd;
+    n_x = n_x < 0 ? 0 : (n_x > per_xcd ? per_xcd : n_x);
+    tail = std::max(tail, (int)(n_x % slots));
+  }
+  if (tail == 0) return 0;
+  int sk = slots / tail;
+  const int forced = env_int("DG_SK_SPLITS", -1);
+  if (forced == 0) return 0;
+  if (forced > 0) sk = forced;
+  if (sk > KB) sk = KB;
+  if (sk > 16) sk = 16;
+  while (sk > 1 && 8LL * tail * sk * ci.bm * ci.bn * (long long)sizeof(float) > (long long)kWorkspaceBytes) --sk;
+  if (sk < 2) return 0;
+  p.sk_splits = sk;
+  p.sk_tail = tail;
+  return grid;
+}
+
 int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   DeviceState* st = nullptr;
   int s = get_device_state(&st);
@@ -208,8 +251,14 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   p.workspace = st->workspace;
   p.workspace_bytes = kWorkspaceBytes;
   p.gate_ok = nullptr;
-  const int grid = plan(mode, ch.cfg, p, st, ch.gated_cfg >= 0);
+  int grid = plan(mode, ch.cfg, p, st, ch.gated_cfg >= 0);
   if (grid == 0) return DG_ERR_UNSUPPORTED;
+  p.sk_splits = 1;
+  p.sk_tail = 0;
+  if (ch.gated_cfg < 0 && ch.splits == 1) {
+    const int sk_grid = plan_split_tail(mode, ch.cfg, p, st);
+    if (sk_grid > 0) grid = sk_grid;
+  }
   if (ch.splits > 1) {
     const long long need = (long long)p.tiles_m * p.tiles_n * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
     if (need > (long long)kWorkspaceBytes)
@@ -231,10 +280,11 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
     e = dg::launch_scale_check(p.sfa, na, p.sfb, nb, st->verdicts, stream);
     if (e == hipSuccess) e = dg::launch_gemm(mode, ch.gated_cfg, pe, grid_e, stream);
   } else if (env_int("DG_LOG", 0)) {
-    std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d kbs=%d grid=%d\n", mode, p.rows,
-                 p.N, p.K, p.G, ci.name, p.splits, p.kbs_per_split, grid);
+    std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d kbs=%d grid=%d tail_splits=%d\n",
+                 mode, p.rows, p.N, p.K, p.G, ci.name, p.splits, p.kbs_per_split, grid, p.sk_splits);
   }
   if (e == hipSuccess) e = dg::launch_gemm(mode, ch.cfg, p, grid, stream);
+  if (e == hipSuccess && p.sk_splits > 1) e = dg::launch_tile_reduce(mode, ch.cfg, p, grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return DG_OK;
 }

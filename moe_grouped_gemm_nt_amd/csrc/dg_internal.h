@@ -33,6 +33,8 @@ struct Params {
   int kbs_per_split;       // K blocks per split (decode kernel only)
   int ab_layout;           // dense: bit 0 = A stored [K][M], bit 1 = B stored [K][N] (0 = nt),
                            // 4 = B packed FP4 (E2M1) with E8M0 scales, sfb int32 [K/128][N]
+  int sk_splits;           // tile kernels: > 1 splits each XCD's tail items over K into this many parts
+  int sk_tail;             // tail items per XCD reserved in the workspace (partial index stride)
   float* d32;              // K-grouped: fp32 D [G][M][N]
   const float* c32;        // K-grouped: fp32 C [G][M][N] or nullptr
 };
@@ -73,6 +75,9 @@ const ConfigInfo& config_info(int cfg);
 // persistently when grid is smaller than the tile count; the decode
 // configuration sizes its own grid from tiles and splits.
 hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
+// Sums the split-tail partial tiles of a tile-kernel launch (p.sk_splits > 1)
+// into D; grid is the tile kernel's grid.
+hipError_t launch_tile_reduce(int mode, int cfg, const Params& p, int grid, hipStream_t stream);
 // K-grouped TN launch on configuration cfg (128x128, 128x256 or 256x256 tiles).
 hipError_t launch_kgrouped(int cfg, const KGroupedParams& p, int grid, hipStream_t stream);
 

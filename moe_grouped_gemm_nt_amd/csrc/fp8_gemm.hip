@@ -184,6 +184,47 @@ splitk_reduce_kernel(Params p) {
     if (row0 + e < p.rows && col < p.N) p.d[(size_t)(row0 + e) * p.N + col] = f32_to_bf16(acc[e] + cv[e]);
 }
 
+// Split-tail reduction of the tile kernels (dense and contiguous calls whose
+// last round of items is split over K): one 256-lane workgroup per 1024
+// elements of a tail item; each lane sums the sk_splits partials of four
+// consecutive columns in split order (deterministic), adds C, rounds and
+// stores the rows that belong to the result.  The item of (XCD x, tail index
+// t) follows the tile kernel's work list: XCD x owns items x*per_xcd ..,
+// whole rounds of `slots` items first, then the tail.
+__global__ void __launch_bounds__(256)
+splitk_tile_reduce_kernel(Params p, int bm, int bn, int slots, int contiguous) {
+  const int chunks = bm * bn / 1024;
+  const int b = blockIdx.x;
+  const int c = b % chunks;
+  const int t = (b / chunks) % p.sk_tail;
+  const int x = b / chunks / p.sk_tail;
+  const int total = p.tiles_m * p.tiles_n;
+  const int per_xcd = (total + 7) / 8;
+  const int w_begin = x * per_xcd;
+  const int n_x = max(0, min(total, w_begin + per_xcd) - w_begin);
+  const int full_x = n_x / slots * slots;
+  if (t >= n_x - full_x) return;
+  int mt, nt;
+  tile_coords(w_begin + full_x + t, p.tiles_m, p.tiles_n, mt, nt);
+  const int e0 = c * 1024 + threadIdx.x * 4;
+  const int row = mt * bm + e0 / bn, col = nt * bn + e0 % bn;
+  if (row >= p.rows) return;
+  if (contiguous) {
+    const int g = p.layout[row];
+    if (g < 0 || g >= p.G) return;
+  }
+  const v4f* part = reinterpret_cast<const v4f*>(p.workspace + ((size_t)(x * p.sk_tail + t) * p.sk_splits) * bm * bn + e0);
+  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.sk_splits; ++s0) acc += __builtin_nontemporal_load(part + (size_t)s0 * (bm * bn / 4));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (col + k >= p.N) break;
+    float v = acc[k];
+    if (p.c) v += bf16_to_f32(p.c[(size_t)row * p.N + col + k]);
+    p.d[(size_t)row * p.N + col + k] = f32_to_bf16(v);
+  }
+}
+
 // ============================================================================
 // narrow kernel (dense shapes with few rows): the whole K per workgroup
 // ============================================================================
@@ -431,6 +472,14 @@ hipError_t launch_kg_cfg(const KGroupedParams& p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_tile_reduce(int mode, int cfg, const Params& p, int grid, hipStream_t stream) {
+  const ConfigInfo& ci = config_info(cfg);
+  const int blocks = 8 * p.sk_tail * (ci.bm * ci.bn / 1024);
+  hipLaunchKernelGGL(splitk_tile_reduce_kernel, dim3(blocks), dim3(256), 0, stream, p, ci.bm, ci.bn, grid / 8,
+                     mode == kContiguous ? 1 : 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_kgrouped(int cfg, const KGroupedParams& p, int grid, hipStream_t stream) {
   switch (cfg) {

@@ -430,13 +430,32 @@ fp8_gemm_nt_kernel(PT p) {
   const int w_end = min(total, w_begin + per_xcd);
   int g_cur = 0;                                   // masked walker state
 
+  // Split tail (dense and 128-row contiguous calls, p.sk_splits > 1): the
+  // XCD's items that do not fill a last round of its workgroups are each
+  // split into sk_splits K ranges, one per workgroup; those write fp32
+  // partial tiles and splitk_tile_reduce_kernel, launched next, sums them.
+  // (not compiled into the 256x256 tile, whose registers are full and whose
+  // calls rarely leave a tail worth splitting)
+  constexpr bool SKOK = (MODE == kDense || (MODE == kContiguous && CBLK == 1)) && LAYOUT == 0 && !E8M0 &&
+                        BM * BN <= 128 * 256;
+  const int n_x = max(0, w_end - w_begin);
+  const int sk_s = SKOK ? p.sk_splits : 1;
+  const int full_x = sk_s > 1 ? n_x / slots * slots : n_x;      // items of whole rounds
+  const int units_x = full_x + (n_x - full_x) * sk_s;
+
   // A contiguous tile whose two 128-row blocks belong to two experts is
   // visited twice, once per expert (pass 0, 1); each visit stores only the
   // rows of its own expert.  The second visit is a repeat of the same item
   // rather than an inner loop, so the K loop keeps a single copy.
   int pass = 0;
-  for (int w = w_begin + slot_id; w < w_end;) {
+  for (int it = slot_id; it < units_x;) {
     // ---- resolve the work item ---------------------------------------------
+    int w = w_begin + it, split = -1, tail_idx = 0;
+    if (it >= full_x) {
+      tail_idx = (it - full_x) / sk_s;
+      w = w_begin + full_x + tail_idx;
+      split = (it - full_x) % sk_s;
+    }
     int group = 0, mt, nt, rows_lim = p.rows;
     if constexpr (MODE == kMasked) {
       while (w >= s_prefix[g_cur + 1]) ++g_cur;
@@ -477,21 +496,26 @@ fp8_gemm_nt_kernel(PT p) {
           pass = 1;                        // visit this tile again for g1
         } else {
           pass = 0;
-          w += slots;
+          it += slots;
         }
-        if (!v0 && !v1) continue;          // uniform across the workgroup
+        if (!v0 && !v1) continue;          // uniform across the workgroup (the reduction skips
+                                           // such rows, so a split unit need not write)
       } else {
-        w += slots;
+        it += slots;
       }
     }
-    if constexpr (MODE == kMasked) w += slots;
+    if constexpr (MODE == kMasked) it += slots;
 
     const int m0 = mt * BM;
     const int n0 = nt * BN;
-    int kbs = KB, kb0 = 0;          // this item's K blocks (K-grouped: the group's)
+    int kbs = KB, kb0 = 0;          // this item's K blocks (K-grouped: the group's; split: its range)
     if constexpr (KG) {
       kb0 = p.k_start[group] / KBLK;
       kbs = p.k_start[group + 1] / KBLK - kb0;
+    }
+    if (split >= 0) {
+      kb0 = split * KB / sk_s;
+      kbs = (split + 1) * KB / sk_s - kb0;
     }
 
     // ---- operand bases -----------------------------------------------------
@@ -527,6 +551,13 @@ fp8_gemm_nt_kernel(PT p) {
       SB += (size_t)kb0 * p.N;          // column scales [K/128][N]
       D32 = p.d32 + (size_t)group * a_rows * p.N;
       if (p.c32) C32 = p.c32 + (size_t)group * a_rows * p.N;
+    }
+    if (SKOK && split >= 0) {
+      // a split's K range: its first K block of A, B and their scales
+      A += (size_t)kb0 * KBLK;
+      B += (size_t)kb0 * KBLK;
+      SA += (size_t)kb0 * a_rows;
+      SB += kb0;                        // B scales [NB][KB]: the row of block nb starts at nb*KB
     }
     int nb = (KG || B4) ? 0 : (n0 + wcol0) / 128;
     nb = nb < NB ? nb : NB - 1;
@@ -785,7 +816,12 @@ fp8_gemm_nt_kernel(PT p) {
           const int row = m0 + wrow0 + i * 16 + g16 * 4 + e;
           const int col = n0 + wcol0 + j * 16 + r16;
           float v = acc[i][j][e];
-          if constexpr (KG) {
+          if (SKOK && split >= 0) {
+            // split unit: the fp32 partial, row-major [BM][BN], to the
+            // workspace slot of (XCD, tail item, split)
+            p.workspace[((size_t)(xcd * p.sk_tail + tail_idx) * sk_s + split) * (BM * BN) +
+                        (wrow0 + i * 16 + g16 * 4 + e) * BN + wcol0 + j * 16 + r16] = v;
+          } else if constexpr (KG) {
             // fp32 result: + C, no rounding beyond the fp32 accumulation
             if (C32) v += C32[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)];
             if (row < rows_lim && col < p.N) D32[(size_t)row * p.N + col] = v;

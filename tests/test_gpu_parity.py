@@ -480,3 +480,52 @@ def test_masked_config4_sampled(dg):
         assert np.all(got[g, m:] == SENTINEL)
         if m:
             assert not np.any(got[g, :m] == SENTINEL)
+
+
+# ---------------------------------------------------------------------------
+# split tail: the last, partly filled round of tile-kernel items split over K
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,sk", [("6", None), ("6", "2"), ("6", "7"), ("6", "0"), ("0", "2"), ("3", "4")])
+def test_dense_split_tail_exact(dg, monkeypatch, cfg, sk):
+    log(f"case: dense split tail, config {cfg}, splits {sk}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
+    p = inputgen.exact_dense(1000, 2112, 1024, seed=12)
+    got = run_dense(dg, p)
+    assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("sk", [None, "3", "8"])
+def test_contiguous_split_tail_exact(dg, monkeypatch, sk):
+    log(f"case: contiguous split tail, splits {sk}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "6")
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
+    G, N, K = 3, 2048, 1024
+    counts = [300, 500, 200]
+    segs = [((c + 127) // 128) * 128 for c in counts]
+    M = sum(segs)
+    layout = np.full(M, -1, dtype=np.int32)
+    off = 0
+    for g, (cnt, sg) in enumerate(zip(counts, segs)):
+        layout[off:off + cnt] = g
+        off += sg
+    base = inputgen.exact_dense(M, N, K, seed=13)
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=90 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=95 + g).sfb for g in range(G)])
+    d = sentinel_like((M, N))
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(base.a), dev(base.sfa), dev(b), dev(sfb),
+                                           bf16_bits_dev(base.c), d, dev(layout))
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_contiguous(base.a, base.sfa, b, sfb, layout, base.c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
+
+
+def test_dense_split_tail_random_tolerance(dg, monkeypatch):
+    log("case: dense split tail, random inputs")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "6")
+    p = inputgen.make_dense(1000, 2112, 3072, 7, 1.0, 0.02, 0.1, False, "random")
+    check_tolerance(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "split tail")
