@@ -10,7 +10,7 @@ same JSON line.  Inputs rotate over enough copies that successive steps
 read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,10]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,11]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
 
@@ -56,6 +56,8 @@ SHAPES = {
     9: ("kgrouped_tn_8x4096x7168_tokens8192", "mfma"),
     # FP8 x FP4: the prefill problem with B in E2M1, one E8M0 scale per 32 K values
     10: ("dense_fp8xfp4_4096x7168x16384", "mfma"),
+    # FP8 x FP4 at the decode shape (B half the bytes of the FP8 one)
+    11: ("dense_fp8xfp4_decode_64x2112x7168", "hbm"),
 }
 LAYOUT_OF = {6: "nn", 7: "tn", 8: "tt"}
 PROBLEM_OF = {6: 3, 7: 3, 8: 3}        # workload index whose generated problem a layout entry reuses
@@ -143,6 +145,8 @@ class Workload:
             self.p = p = inputgen.make_kgrouped(8, 4096, 7168, 8192, seed=0, name=SHAPES[idx][0])
         elif idx == 10:
             self.p = p = inputgen.make_dense_fp4(4096, 7168, 16384, 0, 1.0, 0.02, None, False, SHAPES[idx][0])
+        elif idx == 11:
+            self.p = p = inputgen.make_dense_fp4(64, 2112, 7168, 0, 1.0, 0.02, 0.1, False, SHAPES[idx][0])
         else:
             src = PROBLEM_OF.get(idx, idx)
             if src not in _PROBLEMS:          # the layout entries reuse the prefill problem
@@ -262,7 +266,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10", help="comma-separated 1-based workload indices")
+    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10,11", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")

@@ -109,17 +109,20 @@ int env_int(const char* name, int dflt) {
 }
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
-// kmajor: a dense call with a K-major operand (nn, tn, tt) or an FP4 B, which
-// only the 128x128, 128x256 and 256x256 tile kernels read
-Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, bool kmajor) {
+// ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn), which only the 128x128,
+// 128x256 and 256x256 tile kernels read; 4 an FP4 B, which the decode kernel
+// reads too
+Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
+  const bool kmajor = ab_layout != 0;
+  const bool decode_ok = ab_layout == 0 || ab_layout == 4;
   const int KB = K / 128;
   const long long tiles128 = (long long)((rows + 127) / 128) * ((N + 127) / 128);
   if (!kmajor && mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
     // one 16-row strip and enough 16x48 tiles to occupy half the chip:
     // whole-K tiles, one launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
-  } else if (!kmajor && mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
+  } else if (decode_ok && mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
     // K blocks, all of them in flight at once
@@ -148,7 +151,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, bool km
   // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   const bool forced_ok = !kmajor || forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 ||
-                         forced == dg::kCfg256x256w8;
+                         forced == dg::kCfg256x256w8 || (decode_ok && forced == dg::kCfgDecode);
   if (forced >= 0 && forced < dg::kNumConfigs && forced_ok &&
       ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense)) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
@@ -244,7 +247,7 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
-  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout != 0);
+  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;

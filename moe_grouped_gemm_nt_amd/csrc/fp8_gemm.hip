@@ -16,20 +16,77 @@ namespace {
 constexpr int DBM = 64, DBN = 64;                 // decode tile
 constexpr int DKBS = 8;                           // max K blocks per workgroup
 constexpr int DNW = 4;                            // waves per workgroup
-constexpr int DSLOT = DBM * KBLK + DBN * KBLK + DBM * 4;
-constexpr int DLPB = DBM / 8 + DBN / 8 + 1;       // loads per K block (one wave)
+// one K block's slot: A rows, B rows (FP4: 64 bytes each), A row scales and,
+// for an FP4 B, its packed E8M0 column scales
+template <bool B4> constexpr int dslot() { return DBM * KBLK + DBN * (B4 ? KBLK / 2 : KBLK) + DBM * 4 + (B4 ? DBN * 4 : 0); }
+template <bool B4> constexpr int dlpb() { return DBM / 8 + DBN / (B4 ? 16 : 8) + 1 + B4; }   // loads per K block (one wave)
+constexpr int DSLOT = dslot<false>();
+constexpr int DLPB = dlpb<false>();
 constexpr int DNPW = DKBS / DNW;                  // K blocks per wave
 constexpr int DT = (DBM / 16) * (DBN / 16);       // 16x16 sub-tiles of the tile
 constexpr int DTPW = DT / DNW;                    // sub-tiles each wave finishes
 static_assert(DBM == 64, "one 64-lane load carries the tile's row scales");
 static_assert(DKBS % DNW == 0 && DT % DNW == 0, "blocks and sub-tiles divide among the waves");
 static_assert(DLPB * DNPW < 64, "outstanding loads must fit the 6-bit vmcnt");
-static_assert(DNW * DT * 64 * 16 <= DKBS * DSLOT, "the wave reduction reuses the slot memory");
+static_assert(DNW * DT * 64 * 16 <= DKBS * dslot<true>(), "the wave reduction reuses the slot memory");
 
+// One K block of the FP8 x FP4 decode tile: like mma_block, with B rows of 64
+// bytes (chunk c of row r at c ^ swz4(r)), the A fragment read as K chunks g16
+// and 4+g16 (the fp8 operand's K order against an FP4 operand), and each
+// lane's E8M0 byte for its column and 32-K slice taken from the packed ints.
+template <int SM, int SN>
+__device__ __forceinline__ void mma_block_fp4(const uint8_t* a_rows, const uint8_t* b_rows, const uint32_t* bscale,
+                                              const v4f (&sc)[SM], v4f (&acc)[SM][SN], int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  v8i bf[SN], af[SM];
+  int esb[SN];
+#pragma unroll
+  for (int j = 0; j < SN; ++j) {
+    const int r = j * 16 + r16;
+    const v4i q = *reinterpret_cast<const v4i*>(b_rows + r * (KBLK / 2) + ((g16 ^ swz4(r)) << 4));
+    bf[j] = (v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+    esb[j] = (int)((bscale[r] >> (8 * g16)) & 0xFF);
+  }
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int r = i * 16 + r16;
+    const uint8_t* rp = a_rows + r * KBLK;
+    const v4i lo = *reinterpret_cast<const v4i*>(rp + ((g16 ^ swz(r)) << 4));
+    const v4i hi = *reinterpret_cast<const v4i*>(rp + (((4 + g16) ^ swz(r)) << 4));
+    af[i] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  constexpr int T = SM * SN;
+  constexpr int P = 4;
+  v4f part[P];
+#pragma unroll
+  for (int t = 0; t < T + P - 1; ++t) {
+    if (t < T) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / SN], bf[t % SN], zero, 0, 4, 0, 127, 0,
+                                                                     esb[t % SN]);
+    }
+    const int u = t - (P - 1);
+    if (u >= 0) {
+      v4f& a = acc[u / SN][u % SN];
+      const v4f& q = part[u % P];
+      const v4f& c = sc[u / SN];
+      a.x = __builtin_fmaf(q.x, c.x, a.x);
+      a.y = __builtin_fmaf(q.y, c.y, a.y);
+      a.z = __builtin_fmaf(q.z, c.z, a.z);
+      a.w = __builtin_fmaf(q.w, c.w, a.w);
+    }
+  }
+}
+
+// B4: B holds packed FP4 (E2M1) codes with E8M0 scales per column per 32 K
+// values, packed four to an int32 [K/128][N].
+template <bool B4>
 __global__ void __launch_bounds__(64 * DNW)
 fp8_gemm_nt_decode_kernel(Params p) {
   constexpr int SM = DBM / 16, SN = DBN / 16, T = DT;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * DSLOT];
+  constexpr int SLOT = dslot<B4>(), LPB = dlpb<B4>();
+  constexpr int BROW = B4 ? KBLK / 2 : KBLK;       // bytes of a B row per K block
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,9 +112,9 @@ fp8_gemm_nt_decode_kernel(Params p) {
 
   // this wave's K blocks: kb0 + wave, kb0 + wave + DNW, ...
   const int nown = kbs > wave ? (kbs - wave + DNW - 1) / DNW : 0;
-  float sb[DNPW];
+  float sb[DNPW];                 // the block's B scale (FP4: 1, the MFMA applies the E8M0 scales)
 #pragma unroll
-  for (int j = 0; j < DNPW; ++j) sb[j] = p.sfb[(size_t)nb * KB + min(kb0 + wave + DNW * j, KB - 1)];
+  for (int j = 0; j < DNPW; ++j) sb[j] = B4 ? 1.f : p.sfb[(size_t)nb * KB + min(kb0 + wave + DNW * j, KB - 1)];
 
   // issue every load of this wave's blocks: A (64 rows), B (64 rows), A scales
   const int lr = lane >> 3;
@@ -65,21 +122,35 @@ fp8_gemm_nt_decode_kernel(Params p) {
   for (int j = 0; j < DNPW; ++j) {
     if (j < nown) {
       const int kb = kb0 + wave + DNW * j;
-      const uint32_t slot = smem_base + (uint32_t)((wave + DNW * j) * DSLOT);
+      const uint32_t slot = smem_base + (uint32_t)((wave + DNW * j) * SLOT);
 #pragma unroll
       for (int q = 0; q < DBM / 8; ++q) {
         const int r = q * 8 + lr;
         const int grow = min(m0 + r, p.rows - 1);
         dma_16(p.a + (size_t)grow * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4), slot + q * 1024);
       }
+      if constexpr (B4) {
+        // 16 rows of 64 bytes per instruction: lane l takes row 16q + l/4,
+        // logical chunk (l%4) ^ swz4(row)
 #pragma unroll
-      for (int q = 0; q < DBN / 8; ++q) {
-        const int r = q * 8 + lr;
-        const int gn = min(n0 + r, p.N - 1);
-        dma_16(p.b + (size_t)gn * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4),
-               slot + DBM * KBLK + q * 1024);
+        for (int q = 0; q < DBN / 16; ++q) {
+          const int r = q * 16 + (lane >> 2);
+          const int gn = min(n0 + r, p.N - 1);
+          dma_16(p.b + (size_t)gn * (p.K / 2) + (size_t)kb * BROW + (((lane & 3) ^ swz4(r)) << 4),
+                 slot + DBM * KBLK + q * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < DBN / 8; ++q) {
+          const int r = q * 8 + lr;
+          const int gn = min(n0 + r, p.N - 1);
+          dma_16(p.b + (size_t)gn * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4),
+                 slot + DBM * KBLK + q * 1024);
+        }
       }
-      dma_4(p.sfa + (size_t)kb * p.rows + min(m0 + lane, p.rows - 1), slot + (DBM + DBN) * KBLK);
+      dma_4(p.sfa + (size_t)kb * p.rows + min(m0 + lane, p.rows - 1), slot + DBM * KBLK + DBN * BROW);
+      if constexpr (B4)   // the 64 columns' packed E8M0 scales of this K block
+        dma_4(p.sfb + (size_t)kb * p.N + min(n0 + lane, p.N - 1), slot + DBM * KBLK + DBN * BROW + DBM * 4);
     }
   }
 
@@ -92,13 +163,18 @@ fp8_gemm_nt_decode_kernel(Params p) {
 #pragma unroll
   for (int j = 0; j < DNPW; ++j) {
     if (j < nown) {
-      wait_stages<DLPB, DNPW - 1>(nown - 1 - j);
-      const uint8_t* base = smem + (wave + DNW * j) * DSLOT;
-      const float* sa = reinterpret_cast<const float*>(base + (DBM + DBN) * KBLK);
+      wait_stages<LPB, DNPW - 1>(nown - 1 - j);
+      const uint8_t* base = smem + (wave + DNW * j) * SLOT;
+      const float* sa = reinterpret_cast<const float*>(base + DBM * KBLK + DBN * BROW);
       v4f sc[SM];
 #pragma unroll
       for (int i = 0; i < SM; ++i) sc[i] = *reinterpret_cast<const v4f*>(sa + i * 16 + g16 * 4) * sb[j];
-      mma_block<SM, SN>(base, 0, base + DBM * KBLK, 0, sc, acc, lane);
+      if constexpr (B4)
+        mma_block_fp4<SM, SN>(base, base + DBM * KBLK,
+                              reinterpret_cast<const uint32_t*>(base + DBM * KBLK + DBN * BROW + DBM * 4), sc, acc,
+                              lane);
+      else
+        mma_block<SM, SN>(base, 0, base + DBM * KBLK, 0, sc, acc, lane);
     }
   }
 
@@ -437,7 +513,12 @@ hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
 hipError_t launch_decode(const Params& p, hipStream_t stream) {
   const int items = p.tiles_m * p.tiles_n * p.splits;
   const int grid = ((items + 7) / 8) * 8;
-  hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel, dim3(grid), dim3(64 * DNW), 0, stream, p);
+  if (p.ab_layout == 4)
+    hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<true>, dim3(grid), dim3(64 * DNW), 0, stream, p);
+  else if (p.ab_layout == 0)
+    hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<false>, dim3(grid), dim3(64 * DNW), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(p.tiles_m * p.tiles_n * (DBM / 16) * (DBN / 16)), dim3(64), 0,

@@ -40,12 +40,31 @@ def test_fp4_exact(dg, M, N, K):
     assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
 
 
-@pytest.mark.parametrize("cfg", ["0", "6", "11"])
+@pytest.mark.parametrize("cfg", ["0", "1", "6", "11"])
 def test_fp4_every_tile_config_exact(dg, monkeypatch, cfg):
     log(f"case: fp8 x fp4 exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = inputgen.exact_dense_fp4(400, 592, 640, seed=3)
     assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("splits", ["1", "3", "16"])
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (100, 200, 2048), (1, 64, 128)])
+def test_fp4_decode_splits_exact(dg, monkeypatch, splits, M, N, K):
+    # the decode kernel (64x64 tiles, K split over workgroups) with a forced
+    # split count: one split writes the result itself, more go through the
+    # fp32 partials and the split-K reduction
+    log(f"case: fp8 x fp4 decode exact {M}x{N}x{K}, forced splits {splits}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+    monkeypatch.setenv("DG_FORCE_SPLITS", splits)
+    p = inputgen.exact_dense_fp4(M, N, K, seed=M + 7)
+    assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+def test_fp4_decode_random_tolerance(dg):
+    log("case: fp8 x fp4 random, decode shape 64x2112x7168")
+    p = inputgen.make_dense_fp4(64, 2112, 7168, 11, 1.0, 0.02, 0.1, False)
+    check_tolerance(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c), "fp4 decode")
 
 
 @pytest.mark.parametrize("pow2", [True, False])
