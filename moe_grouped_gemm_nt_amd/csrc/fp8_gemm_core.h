@@ -774,7 +774,19 @@ fp8_gemm_nt_kernel(PT p) {
 #pragma unroll
       for (int u = 0; u < NSLOT - 1; ++u) issue(min(u, kbs - 1), u);
     }
-    if constexpr (E8M0) {
+    // A wave whose rows all lie past the item's valid rows (a masked group's
+    // last m-tile, the end of A) only issues its share of the loads and meets
+    // the barriers: its MFMAs would produce nothing that is stored, and
+    // skipping them frees its SIMD for the wave sharing it.
+    const bool idle = __builtin_amdgcn_readfirstlane(m0 + wrow0 >= rows_lim ? 1 : 0) != 0;
+    if (idle) {
+      const int steps = E8M0 ? kbs : (kbs + NSLOT - 1) / NSLOT * NSLOT;
+      for (int i = 0; i < steps; ++i) {
+        wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
+        bare_barrier();
+        issue(min(i + NSLOT - 1, kbs - 1), (i + NSLOT - 1) % NSLOT);
+      }
+    } else if constexpr (E8M0) {
       for (int i0 = 0; i0 < kbs; i0 += NSLOT) {
         static_for<NSLOT>([&](auto u_const) {
           constexpr int u = decltype(u_const)::value;
