@@ -211,7 +211,7 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
   const dg::ConfigInfo& ci = dg::config_info(cfg);
   p.sk_splits = 1;
   p.sk_tail = 0;
-  if (mode == dg::kMasked || p.ab_layout != 0 || ci.bm * ci.bn > 128 * 256) return 0;
+  if (mode == dg::kMasked || ci.bm * ci.bn > 128 * 256) return 0;
   if (mode == dg::kContiguous && ci.bm > 128) return 0;
   if (cfg == dg::kCfgDecode || cfg == dg::kCfgNarrow || cfg == dg::kCfgE8_128x256 || cfg == dg::kCfgWs_128x256 ||
       cfg == dg::kCfgE8_256x256)

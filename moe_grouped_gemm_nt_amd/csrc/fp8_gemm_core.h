@@ -436,8 +436,7 @@ fp8_gemm_nt_kernel(PT p) {
   // partial tiles and splitk_tile_reduce_kernel, launched next, sums them.
   // (not compiled into the 256x256 tile, whose registers are full and whose
   // calls rarely leave a tail worth splitting)
-  constexpr bool SKOK = (MODE == kDense || (MODE == kContiguous && CBLK == 1)) && LAYOUT == 0 && !E8M0 &&
-                        BM * BN <= 128 * 256;
+  constexpr bool SKOK = (MODE == kDense || (MODE == kContiguous && CBLK == 1)) && !E8M0 && BM * BN <= 128 * 256;
   const int n_x = max(0, w_end - w_begin);
   const int sk_s = SKOK ? p.sk_splits : 1;
   const int full_x = sk_s > 1 ? n_x / slots * slots : n_x;      // items of whole rounds
@@ -554,10 +553,11 @@ fp8_gemm_nt_kernel(PT p) {
     }
     if (SKOK && split >= 0) {
       // a split's K range: its first K block of A, B and their scales
-      A += (size_t)kb0 * KBLK;
-      B += (size_t)kb0 * KBLK;
+      A += TA ? (size_t)kb0 * KBLK * a_rows : (size_t)kb0 * KBLK;
+      B += TB ? (size_t)kb0 * KBLK * p.N : (size_t)kb0 * S::B_ROW;
       SA += (size_t)kb0 * a_rows;
-      SB += kb0;                        // B scales [NB][KB]: the row of block nb starts at nb*KB
+      // B scales: FP4 int32 [K/128][N]; otherwise [NB][KB], block nb's row at nb*KB
+      SB += B4 ? (size_t)kb0 * p.N : (size_t)kb0;
     }
     int nb = (KG || B4) ? 0 : (n0 + wcol0) / 128;
     nb = nb < NB ? nb : NB - 1;

@@ -48,6 +48,17 @@ def test_fp4_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
 
 
+@pytest.mark.parametrize("cfg,sk", [("0", None), ("0", "16"), ("6", "3")])
+def test_fp4_split_tail_exact(dg, monkeypatch, cfg, sk):
+    # the tile kernels' last partial round split over K, with an FP4 B
+    log(f"case: fp8 x fp4 split tail, config {cfg}, splits {sk}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
+    p = inputgen.exact_dense_fp4(1000, 2112, 1024, seed=15)
+    assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
 @pytest.mark.parametrize("splits", ["1", "3", "16"])
 @pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (100, 200, 2048), (1, 64, 128)])
 def test_fp4_decode_splits_exact(dg, monkeypatch, splits, M, N, K):
@@ -94,11 +105,13 @@ def _fp4_experts(G, N, K, seed):
     return np.stack([q.b for q in ps]), np.stack([q.sfb for q in ps])
 
 
-@pytest.mark.parametrize("cfg", [None, "0", "6", "11"])
-def test_fp4_contiguous_exact(dg, monkeypatch, cfg):
-    log(f"case: fp8 x fp4 contiguous exact, config {cfg}")
+@pytest.mark.parametrize("cfg,sk", [(None, None), ("0", None), ("6", None), ("11", None), ("0", "5"), ("6", "3")])
+def test_fp4_contiguous_exact(dg, monkeypatch, cfg, sk):
+    log(f"case: fp8 x fp4 contiguous exact, config {cfg}, split tail {sk}")
     if cfg is not None:
         monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
     G, N, K = 3, 272, 512
     counts = [200, 5, 300]
     segs = [((c + 127) // 128) * 128 for c in counts]

@@ -104,3 +104,25 @@ def test_layout_sizes_rejected(dg):
         assert e.value.status == -2
     got, a, b = run_layout(dg, "nn", p)                       # nn with M = 40 is fine
     assert np.array_equal(got, oracle.gemm_layout("nn", a, p.sfa, b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("cfg,sk", [("0", None), ("0", "16"), ("6", None), ("6", "3")])
+def test_layout_split_tail_exact(dg, monkeypatch, layout, cfg, sk):
+    # the items of a last partial round split over K (fp32 partials, then the
+    # split reduction), with K-major operands
+    log(f"case: {layout} split tail, config {cfg}, splits {sk}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
+    p = inputgen.exact_dense(992, 2112, 1024, seed=14)
+    got, a, b = run_layout(dg, layout, p)
+    assert np.array_equal(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_layout_decode_shape_random_tolerance(dg, layout):
+    log(f"case: {layout} random, decode shape 64x2112x7168")
+    p = inputgen.make_dense(64, 2112, 7168, 5, 1.0, 0.02, 0.1, True, "random")
+    got, a, b = run_layout(dg, layout, p)
+    check_tolerance(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c), layout)
