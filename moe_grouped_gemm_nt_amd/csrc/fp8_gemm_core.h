@@ -819,6 +819,19 @@ fp8_gemm_nt_kernel(PT p) {
     // One element at a time in accumulator order (i, j, e): each accumulator
     // tuple is consumed whole, which keeps register pressure low enough that
     // the accumulators are never split or spilled around the K loop.
+    // Contiguous: the lane's rows (strip i, quad row e: bit 4i+e) that belong
+    // to this item's expert, read from grouped_layout once, all loads together.
+    static_assert(S::SM * 4 <= 32, "row mask bits");
+    uint32_t row_ok = ~0u;
+    if constexpr (MODE == kContiguous) {
+      int ids[S::SM * 4];
+#pragma unroll
+      for (int q = 0; q < S::SM * 4; ++q)
+        ids[q] = p.layout[min(m0 + wrow0 + (q / 4) * 16 + g16 * 4 + q % 4, p.rows - 1)];
+      row_ok = 0;
+#pragma unroll
+      for (int q = 0; q < S::SM * 4; ++q) row_ok |= (ids[q] == group ? 1u : 0u) << q;
+    }
 #pragma unroll
     for (int i = 0; i < S::SM; ++i)
 #pragma unroll
@@ -839,8 +852,7 @@ fp8_gemm_nt_kernel(PT p) {
             if (row < rows_lim && col < p.N) D32[(size_t)row * p.N + col] = v;
           } else {
             if (C) v += bf16_to_f32(C[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
-            if (row < rows_lim && col < p.N &&
-                (MODE != kContiguous || p.layout[min(row, p.rows - 1)] == group))
+            if (row < rows_lim && col < p.N && ((row_ok >> (i * 4 + e)) & 1))
               D[(size_t)row * p.N + col] = f32_to_bf16(v);
           }
         }
