@@ -135,6 +135,13 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its global stores (__syncthreads would also wait for every store in flight)
+__device__ __forceinline__ void lds_barrier() {
+  wait_vm_lgkm0<63>();
+  bare_barrier();
+}
+
 // Reads the MFMA operand fragment of one 16-row strip: lane l takes row l%16
 // of the strip and the 32-byte K slice l/16 of it (logical 16-byte chunks
 // 2*(l/16) and 2*(l/16)+1, stored at their swizzled positions).
@@ -486,9 +493,9 @@ fp8_gemm_nt_kernel(PT p) {
           for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
           if (lane == 0) s_group[wave] = best;
         }
-        __syncthreads();
+        lds_barrier();
         const int g0 = s_group[0], g1 = s_group[CBLK - 1];
-        __syncthreads();
+        lds_barrier();
         const bool v0 = g0 >= 0 && g0 < p.G, v1 = g1 >= 0 && g1 < p.G;
         group = pass == 0 && v0 ? g0 : g1;
         if (pass == 0 && v0 && v1 && g0 != g1) {
@@ -856,11 +863,12 @@ fp8_gemm_nt_kernel(PT p) {
               D[(size_t)row * p.N + col] = f32_to_bf16(v);
           }
         }
-    // the next item reuses the LDS ring; nothing of this item stays in flight
-    // (without this the compiler assumes a load of this item may still be
-    // pending in the next item's K loop and waits for every load there)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // The next item reuses the LDS ring once every wave is past its K loop.
+    // The epilogue's stores stay in flight while the next item's first loads
+    // are issued: a wait for "at most n operations outstanding" in its K loop
+    // still covers the block it needs, because loads complete in issue order
+    // and stores only add to the count.
+    lds_barrier();
   }
 }
 
