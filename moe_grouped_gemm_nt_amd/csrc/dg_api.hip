@@ -248,6 +248,9 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   if (s != DG_OK) return s;
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
   Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout);
+  // With a C the 128x256 tile is preferred: it reads C into its accumulators
+  // before the K loop, while the 256x256 tile must read it between its stores.
+  if (ch.cfg == dg::kCfg256x256w8 && p.c && env_int("DG_FORCE_CONFIG", -1) < 0) ch.cfg = dg::kCfg128x256w8;
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
@@ -419,7 +422,11 @@ extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* s
   // the largest tile that still gives every CU a work item (as for dense calls)
   const long long t256 = (long long)num_groups * ((M + 255) / 256) * ((N + 255) / 256);
   const long long t128x256 = (long long)num_groups * ((M + 127) / 128) * ((N + 255) / 256);
-  int cfg = t256 >= st->num_cus ? dg::kCfg256x256w8 : t128x256 >= st->num_cus ? dg::kCfg128x256w8 : dg::kCfg128x128;
+  // With a C the 128x256 tile is preferred: it reads C into its accumulators
+  // before the K loop, while the 256x256 tile must read it between its stores.
+  int cfg = t256 >= st->num_cus && !c ? dg::kCfg256x256w8
+            : t128x256 >= st->num_cus ? dg::kCfg128x256w8
+                                      : dg::kCfg128x128;
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 || forced == dg::kCfg256x256w8) cfg = forced;
   const dg::ConfigInfo& ci = dg::config_info(cfg);

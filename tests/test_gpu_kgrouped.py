@@ -85,9 +85,13 @@ def test_kgrouped_without_c_and_in_place(dg):
     assert np.array_equal(d.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("pow2", [True, False])
-def test_kgrouped_random_bound(dg, pow2):
-    log(f"case: k-grouped random, pow2={pow2}")
+@pytest.mark.parametrize("pow2,cfg", [(True, None), (False, None), (False, "0"), (False, "6"), (False, "11")])
+def test_kgrouped_random_bound(dg, monkeypatch, pow2, cfg):
+    # with an fp32 C: the tiles up to 128x256 start their accumulators at C,
+    # the 256x256 tile adds it after the K loop
+    log(f"case: k-grouped random, pow2={pow2}, config {cfg}")
+    if cfg is not None:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = inputgen.make_kgrouped(4, 512, 768, 3000, seed=7, pow2=pow2, with_c=True)
     got = run_kg(dg, p)
     rel = check_bound(got, p)
