@@ -292,13 +292,15 @@ splitk_tile_reduce_kernel(Params p, int bm, int bn, int slots, int contiguous) {
   const v4f* part = reinterpret_cast<const v4f*>(p.workspace + ((size_t)(x * p.sk_tail + t) * p.sk_splits) * bm * bn + e0);
   v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.sk_splits; ++s0) acc += __builtin_nontemporal_load(part + (size_t)s0 * (bm * bn / 4));
+  // C first, then the stores (a load after a store waits for the store too)
+  if (p.c) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (col + k >= p.N) break;
-    float v = acc[k];
-    if (p.c) v += bf16_to_f32(p.c[(size_t)row * p.N + col + k]);
-    p.d[(size_t)row * p.N + col + k] = f32_to_bf16(v);
+    for (int k = 0; k < 4; ++k)
+      if (col + k < p.N) acc[k] += bf16_to_f32(p.c[(size_t)row * p.N + col + k]);
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (col + k < p.N) p.d[(size_t)row * p.N + col + k] = f32_to_bf16(acc[k]);
 }
 
 // ============================================================================
@@ -420,15 +422,22 @@ fp8_gemm_nt_narrow_kernel(Params p) {
   for (int w = 0; w < 3; ++w)
 #pragma unroll
     for (int c = 0; c < SN; ++c) acc[0][c] += red[(w * SN + c) * 64 + lane];
+  // C first, then the stores (a load after a store waits for the store too)
+  if (p.c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c = 0; c < SN; ++c)
+        acc[0][c][e] += bf16_to_f32(p.c[(size_t)min(m0 + 4 * g16 + e, p.rows - 1) * p.N +
+                                        min(n0 + 16 * c + r16, p.N - 1)]);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = m0 + 4 * g16 + e;
 #pragma unroll
     for (int c = 0; c < SN; ++c) {
       const int col = n0 + 16 * c + r16;
-      float v = acc[0][c][e];
-      if (p.c) v += bf16_to_f32(p.c[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
-      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(v);
+      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(acc[0][c][e]);
     }
   }
 }

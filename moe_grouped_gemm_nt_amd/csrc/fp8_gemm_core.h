@@ -317,10 +317,6 @@ __device__ __forceinline__ float lds_f32(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
 }
 
-// What the tile kernels read as C when a call has none.
-__device__ const float kZeroF32 = 0.f;
-__device__ const uint16_t kZeroBF16 = 0;
-
 // Direct global->LDS load with a uniform 64-bit base in SGPRs and a 32-bit
 // per-lane byte offset.
 __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
@@ -781,37 +777,10 @@ fp8_gemm_nt_kernel(PT p) {
 #pragma unroll
       for (int u = 0; u < NSLOT - 1; ++u) issue(min(u, kbs - 1), u);
     }
-    // Tiles up to 128x256 start the accumulators at C: its loads go straight
-    // into the accumulator registers while the ring's first blocks are in
-    // flight, where read in the epilogue each load would wait for every store
-    // issued before it.  Without a C (and in split units, whose C the split
-    // reduction adds) every lane reads the one zero word, so the code is the
-    // same either way (a branch here would split the accumulators across two
-    // paths).  The 256x256 tile and the MFMA-scaled kernels (accumulators in
-    // AGPRs) have no registers for this and add C in the epilogue.
-    constexpr bool C_FIRST = BM * BN <= 128 * 256 && !E8M0;
-    const bool split_unit = SKOK && split >= 0;
-    const bool c_in = !split_unit && (KG ? C32 != nullptr : C != nullptr);
-    if constexpr (C_FIRST) {
-      const float* c32_src = c_in && KG ? C32 : &kZeroF32;
-      const uint16_t* c16_src = c_in && !KG ? C : &kZeroBF16;
 #pragma unroll
-      for (int i = 0; i < S::SM; ++i)
+    for (int i = 0; i < S::SM; ++i)
 #pragma unroll
-        for (int j = 0; j < S::SN; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const size_t off = (size_t)min(m0 + wrow0 + i * 16 + g16 * 4 + e, p.rows - 1) * p.N +
-                               min(n0 + wcol0 + j * 16 + r16, p.N - 1);
-            if constexpr (KG) acc[i][j][e] = c32_src[c_in ? off : 0];
-            else acc[i][j][e] = bf16_to_f32(c16_src[c_in ? off : 0]);
-          }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::SM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    }
+      for (int j = 0; j < S::SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     // A wave whose rows all lie past the item's valid rows (a masked group's
     // last m-tile, the end of A) only issues its share of the loads and meets
@@ -871,8 +840,30 @@ fp8_gemm_nt_kernel(PT p) {
 #pragma unroll
       for (int q = 0; q < S::SM * 4; ++q) row_ok |= (ids[q] == group ? 1u : 0u) << q;
     }
+    // C is read a strip at a time, strip i+1 before the stores of strip i: a
+    // load issued after a store can only be waited for together with that
+    // store (one in-order count covers both), so reading C element by element
+    // between the stores would wait for every earlier store.  The 256x256
+    // tile and the MFMA-scaled kernels have no registers for the two strip
+    // buffers and read C per element.
+    const bool split_unit = SKOK && split >= 0;
+    const bool c_in = !split_unit && (KG ? C32 != nullptr : C != nullptr);
+    constexpr bool C_PIPE = BM * BN <= 128 * 256 && !E8M0;
+    float cv[2][S::SN * 4];
+    auto c_at = [&](int row, int col) {
+      const size_t off = (size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1);
+      return KG ? C32[off] : bf16_to_f32(C[off]);
+    };
+    auto load_c = [&](int i, float (&dst)[S::SN * 4]) {
+#pragma unroll
+      for (int j = 0; j < S::SN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[j * 4 + e] = c_at(m0 + wrow0 + i * 16 + g16 * 4 + e, n0 + wcol0 + j * 16 + r16);
+    };
+    if (C_PIPE && c_in) load_c(0, cv[0]);
 #pragma unroll
     for (int i = 0; i < S::SM; ++i) {
+      if (C_PIPE && c_in && i + 1 < S::SM) load_c(i + 1, cv[(i + 1) % 2]);
 #pragma unroll
       for (int j = 0; j < S::SN; ++j)
 #pragma unroll
@@ -886,10 +877,7 @@ fp8_gemm_nt_kernel(PT p) {
             p.workspace[((size_t)(xcd * p.sk_tail + tail_idx) * sk_s + split) * (BM * BN) +
                         (wrow0 + i * 16 + g16 * 4 + e) * BN + wcol0 + j * 16 + r16] = v;
           } else {
-            if (!C_FIRST && c_in) {
-              const size_t off = (size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1);
-              v += KG ? C32[off] : bf16_to_f32(C[off]);
-            }
+            if (c_in) v += C_PIPE ? cv[i % 2][j * 4 + e] : c_at(row, col);
             if constexpr (KG) {
               // fp32 result + C: no rounding beyond the fp32 accumulation
               if (row < rows_lim && col < p.N) D32[(size_t)row * p.N + col] = v;
