@@ -109,20 +109,19 @@ int env_int(const char* name, int dflt) {
 }
 
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
-// ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn), which only the 128x128,
-// 128x256 and 256x256 tile kernels read; 4 an FP4 B, which the decode kernel
-// reads too
+// ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn); 4 an FP4 B.  The
+// other layouts are read by the 128x128, 128x256 and 256x256 tile kernels and
+// the decode kernel only.
 Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const bool kmajor = ab_layout != 0;
-  const bool decode_ok = ab_layout == 0 || ab_layout == 4;
   const int KB = K / 128;
   const long long tiles128 = (long long)((rows + 127) / 128) * ((N + 127) / 128);
   if (!kmajor && mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
     // one 16-row strip and enough 16x48 tiles to occupy half the chip:
     // whole-K tiles, one launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
-  } else if (decode_ok && mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
+  } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
     // K blocks, all of them in flight at once
@@ -151,7 +150,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
   // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   const bool forced_ok = !kmajor || forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 ||
-                         forced == dg::kCfg256x256w8 || (decode_ok && forced == dg::kCfgDecode);
+                         forced == dg::kCfg256x256w8 || forced == dg::kCfgDecode;
   if (forced >= 0 && forced < dg::kNumConfigs && forced_ok &&
       ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense)) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {

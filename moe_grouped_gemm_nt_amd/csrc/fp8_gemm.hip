@@ -78,11 +78,54 @@ __device__ __forceinline__ void mma_block_fp4(const uint8_t* a_rows, const uint8
   }
 }
 
-// B4: B holds packed FP4 (E2M1) codes with E8M0 scales per column per 32 K
-// values, packed four to an int32 [K/128][N].
-template <bool B4>
+// One K block of the decode tile with a K-major operand (TA: A stored
+// [K][M]; TB: B stored [K][N]): such an operand's block sits in LDS in the
+// octet layout of kmajor_slot<64> and its fragments are gathered with the
+// transposing LDS reads of kmajor_frag; the other operand is read as in
+// mma_block.  a_lds / b_lds are the LDS addresses of the same rows.
+template <int SM, int SN, bool TA, bool TB>
+__device__ __forceinline__ void mma_block_kmajor(const uint8_t* a_rows, uint32_t a_lds, const uint8_t* b_rows,
+                                                 uint32_t b_lds, const v4f (&sc)[SM], v4f (&acc)[SM][SN], int lane) {
+  const int g16 = lane >> 4, r16 = lane & 15;
+  v8i bf[SN], af[SM];
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+    bf[j] = TB ? kmajor_frag<DBN>(b_lds + kmajor_frag_base<DBN>(0, lane, j & 1) + 128 * j)
+               : lds_fragment(b_rows, j * 16 + r16, g16);
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+    af[i] = TA ? kmajor_frag<DBM>(a_lds + kmajor_frag_base<DBM>(0, lane, i & 1) + 128 * i)
+               : lds_fragment(a_rows, i * 16 + r16, g16);
+  constexpr int T = SM * SN;
+  constexpr int P = 4;
+  v4f part[P];
+#pragma unroll
+  for (int t = 0; t < T + P - 1; ++t) {
+    if (t < T) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      part[t % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[t / SN], bf[t % SN], zero, 0, 0, 0, 0, 0, 0);
+    }
+    const int u = t - (P - 1);
+    if (u >= 0) {
+      v4f& a = acc[u / SN][u % SN];
+      const v4f& q = part[u % P];
+      const v4f& c = sc[u / SN];
+      a.x = __builtin_fmaf(q.x, c.x, a.x);
+      a.y = __builtin_fmaf(q.y, c.y, a.y);
+      a.z = __builtin_fmaf(q.z, c.z, a.z);
+      a.w = __builtin_fmaf(q.w, c.w, a.w);
+    }
+  }
+}
+
+// LAYOUT: 0 nt; 1 tt (A stored [K][M]); 2 nn (B stored [K][N]); 3 tn (both);
+// 4 FP8 x FP4: B holds packed FP4 (E2M1) codes with E8M0 scales per column per
+// 32 K values, packed four to an int32 [K/128][N].
+template <int LAYOUT>
 __global__ void __launch_bounds__(64 * DNW)
 fp8_gemm_nt_decode_kernel(Params p) {
+  constexpr bool B4 = LAYOUT == 4;
+  constexpr bool TA = !B4 && (LAYOUT & 1), TB = !B4 && (LAYOUT & 2);
   constexpr int SM = DBM / 16, SN = DBN / 16, T = DT;
   constexpr int SLOT = dslot<B4>(), LPB = dlpb<B4>();
   constexpr int BROW = B4 ? KBLK / 2 : KBLK;       // bytes of a B row per K block
@@ -123,13 +166,32 @@ fp8_gemm_nt_decode_kernel(Params p) {
     if (j < nown) {
       const int kb = kb0 + wave + DNW * j;
       const uint32_t slot = smem_base + (uint32_t)((wave + DNW * j) * SLOT);
+      if constexpr (TA) {
+        // A stored [K][M]: 128 K rows of the tile's 64 columns in octets
+        // (kmajor_slot); chunks past M re-read the last 16 columns
 #pragma unroll
-      for (int q = 0; q < DBM / 8; ++q) {
-        const int r = q * 8 + lr;
-        const int grow = min(m0 + r, p.rows - 1);
-        dma_16(p.a + (size_t)grow * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4), slot + q * 1024);
+        for (int q = 0; q < DBM / 8; ++q) {
+          int kr, c;
+          kmajor_slot<DBM>(64 * q + lane, kr, c);
+          dma_16(p.a + (size_t)(kb * KBLK + kr) * p.rows + min(m0 + 16 * c, p.rows - 16), slot + q * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < DBM / 8; ++q) {
+          const int r = q * 8 + lr;
+          const int grow = min(m0 + r, p.rows - 1);
+          dma_16(p.a + (size_t)grow * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4), slot + q * 1024);
+        }
       }
-      if constexpr (B4) {
+      if constexpr (TB) {
+        // B stored [K][N], as A above
+#pragma unroll
+        for (int q = 0; q < DBN / 8; ++q) {
+          int kr, c;
+          kmajor_slot<DBN>(64 * q + lane, kr, c);
+          dma_16(p.b + (size_t)(kb * KBLK + kr) * p.N + min(n0 + 16 * c, p.N - 16), slot + DBM * KBLK + q * 1024);
+        }
+      } else if constexpr (B4) {
         // 16 rows of 64 bytes per instruction: lane l takes row 16q + l/4,
         // logical chunk (l%4) ^ swz4(row)
 #pragma unroll
@@ -173,6 +235,9 @@ fp8_gemm_nt_decode_kernel(Params p) {
         mma_block_fp4<SM, SN>(base, base + DBM * KBLK,
                               reinterpret_cast<const uint32_t*>(base + DBM * KBLK + DBN * BROW + DBM * 4), sc, acc,
                               lane);
+      else if constexpr (TA || TB)
+        mma_block_kmajor<SM, SN, TA, TB>(base, lds_u32(base), base + DBM * KBLK, lds_u32(base + DBM * KBLK), sc, acc,
+                                         lane);
       else
         mma_block<SM, SN>(base, 0, base + DBM * KBLK, 0, sc, acc, lane);
     }
@@ -522,12 +587,14 @@ hipError_t launch_cfg(int mode, const Params& p, int grid, hipStream_t stream) {
 hipError_t launch_decode(const Params& p, hipStream_t stream) {
   const int items = p.tiles_m * p.tiles_n * p.splits;
   const int grid = ((items + 7) / 8) * 8;
-  if (p.ab_layout == 4)
-    hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<true>, dim3(grid), dim3(64 * DNW), 0, stream, p);
-  else if (p.ab_layout == 0)
-    hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<false>, dim3(grid), dim3(64 * DNW), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
+  switch (p.ab_layout) {
+    case 0: hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<0>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<1>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<2>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<3>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(fp8_gemm_nt_decode_kernel<4>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(p.tiles_m * p.tiles_n * (DBM / 16) * (DBN / 16)), dim3(64), 0,

@@ -59,7 +59,7 @@ def test_layout_exact(dg, layout, M, N, K):
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
-@pytest.mark.parametrize("cfg", ["0", "6", "11"])
+@pytest.mark.parametrize("cfg", ["0", "1", "6", "11"])
 def test_layout_every_tile_config_exact(dg, monkeypatch, layout, cfg):
     log(f"case: {layout} exact, forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
@@ -126,3 +126,18 @@ def test_layout_decode_shape_random_tolerance(dg, layout):
     p = inputgen.make_dense(64, 2112, 7168, 5, 1.0, 0.02, 0.1, True, "random")
     got, a, b = run_layout(dg, layout, p)
     check_tolerance(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c), layout)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("splits", ["1", "3", "16"])
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (96, 160, 2048), (16, 16, 128)])
+def test_layout_decode_kernel_exact(dg, monkeypatch, layout, splits, M, N, K):
+    # the decode kernel (64x64 tiles, K split over workgroups) with K-major
+    # operands staged in octets and read with transposing LDS reads; one split
+    # writes D itself, more go through the fp32 partials and the reduction
+    log(f"case: {layout} decode kernel exact {M}x{N}x{K}, forced splits {splits}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+    monkeypatch.setenv("DG_FORCE_SPLITS", splits)
+    p = inputgen.exact_dense(M, N, K, seed=M + K)
+    got, a, b = run_layout(dg, layout, p)
+    assert np.array_equal(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c))
