@@ -124,12 +124,17 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
   } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
-    // K blocks, all of them in flight at once
+    // K blocks, all of them in flight at once, and at least 4
     ch.cfg = dg::kCfgDecode;
     const int tiles = ((rows + 63) / 64) * ((N + 63) / 64);
     int splits = (KB + 7) / 8;
     const int fill = num_cus / (tiles > 0 ? tiles : 1);
-    if (fill > splits) splits = fill < KB ? fill : KB;
+    // up to 8 K blocks one split does the call in one launch, which measured
+    // faster than any split count (the reduction is a second launch); beyond,
+    // splits of fewer than 4 blocks measured slower than fewer, longer ones
+    // (the partials to reduce grow with the split count)
+    const int cap = KB / 4;
+    if (KB > 8 && fill > splits) splits = fill < cap ? fill : cap;
     ch.splits = splits;
   } else {
     // the largest tile that still gives every CU a tile: per K block a CU
