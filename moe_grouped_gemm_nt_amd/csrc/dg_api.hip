@@ -108,6 +108,15 @@ int env_int(const char* name, int dflt) {
   return v && *v ? std::atoi(v) : dflt;
 }
 
+// The decode kernel runs one workgroup per CU; with a long K its splits (at
+// most 8 K blocks each) can need several rounds of the chip, and measured
+// beyond about two and a quarter rounds the tile kernels (with their split
+// tail) were faster.  Its fp32 partials must also fit the workspace.
+bool decode_fits(long long tiles64, int KB, int num_cus) {
+  const long long wgs = tiles64 * ((KB + 7) / 8);
+  return wgs <= 2LL * num_cus + num_cus / 4 && wgs * 64 * 64 * (long long)sizeof(float) <= (long long)kWorkspaceBytes;
+}
+
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 // ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn); 4 an FP4 B.  The
 // other layouts are read by the 128x128, 128x256 and 256x256 tile kernels and
@@ -121,7 +130,8 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
     // one 16-row strip and enough 16x48 tiles to occupy half the chip:
     // whole-K tiles, one launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
-  } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus) {
+  } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus &&
+             decode_fits(((long long)(rows + 63) / 64) * ((N + 63) / 64), KB, num_cus)) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
     // K blocks, all of them in flight at once, and at least 4

@@ -529,3 +529,15 @@ def test_dense_split_tail_random_tolerance(dg, monkeypatch):
     monkeypatch.setenv("DG_FORCE_CONFIG", "6")
     p = inputgen.make_dense(1000, 2112, 3072, 7, 1.0, 0.02, 0.1, False, "random")
     check_tolerance(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c), "split tail")
+
+
+def test_dense_long_k_wide_n_decode_shape(dg):
+    # 64 rows, N = 16000, K = 16384: few enough 128x128 tiles for the decode
+    # kernel's range, but its K splits would need more than two rounds of the
+    # chip and more fp32 partials than the workspace holds, so the call takes
+    # a tile kernel
+    log("case: dense 64x16000x16384 (decode-shaped, long K, wide N), sampled rows")
+    p = inputgen.make_dense(64, 16000, 16384, 17, 1.0, 0.02, 0.1, True, "wide")
+    got = run_dense(dg, p)
+    rows = np.array([0, 1, 31, 32, 63])
+    check_tolerance(got[rows], oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c, rows=rows), "64x16000x16384")
