@@ -37,6 +37,12 @@
  * on the device.  Faults inside a kernel surface at the caller's next
  * synchronisation, as for any HIP kernel.
  *
+ * All calls on one device share its split-K workspace (fp32 partial tiles)
+ * and its scale-check results.  Calls enqueued on one stream, or ordered
+ * across streams by events, are safe; calls that may run at the same time on
+ * different streams of one device race on that memory and must be ordered by
+ * the caller.
+ *
  * Errors: an invalid argument returns DG_ERR_INVALID_ARG and launches nothing;
  * a shape the kernels do not handle returns DG_ERR_UNSUPPORTED; a failing HIP
  * call returns DG_ERR_HIP.  dg_last_error() then describes the failure (per
