@@ -10,7 +10,7 @@ same JSON line.  Inputs rotate over enough copies that successive steps
 read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,11]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,13]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
 
@@ -58,9 +58,15 @@ SHAPES = {
     10: ("dense_fp8xfp4_4096x7168x16384", "mfma"),
     # FP8 x FP4 at the decode shape (B half the bytes of the FP8 one)
     11: ("dense_fp8xfp4_decode_64x2112x7168", "hbm"),
+    # the contiguous and masked problems (power-of-two scales) through the
+    # kernels that apply the scales in the MFMA from their E8M0 codes, behind
+    # the on-device scale check (not the default choice: measured slower)
+    12: ("contiguous_8x4096x7168_rows8192_e8m0", "mfma"),
+    13: ("masked_32x256x4096x7168_e8m0", "hbm"),
 }
 LAYOUT_OF = {6: "nn", 7: "tn", 8: "tt"}
-PROBLEM_OF = {6: 3, 7: 3, 8: 3}        # workload index whose generated problem a layout entry reuses
+PROBLEM_OF = {6: 3, 7: 3, 8: 3, 12: 4, 13: 5}   # workload index whose generated problem an entry reuses
+FORCED_CONFIG = {12: "8", 13: "10"}     # kernel configuration an entry selects (DG_FORCE_CONFIG)
 
 
 def log(msg):
@@ -154,6 +160,7 @@ class Workload:
             self.p = p = _PROBLEMS[src]
         self.name, self.bound = SHAPES[idx]
         self.layout = LAYOUT_OF.get(idx, "nt")
+        self.forced = FORCED_CONFIG.get(idx)
         self.flops = p.flops
         self.bytes = algorithmic_bytes(p)
         per_copy = p.a.nbytes + p.b.nbytes
@@ -194,6 +201,12 @@ class Workload:
     def launch(self, i):
         s = self.sets[i % self.copies]
         dg = self.dg
+        # the configuration is chosen on the host at each call (and recorded
+        # when a graph is captured)
+        if self.forced is not None:
+            os.environ["DG_FORCE_CONFIG"] = self.forced
+        else:
+            os.environ.pop("DG_FORCE_CONFIG", None)
         if self.kind == "Dense":
             getattr(dg, "dg_fp8_gemm_" + self.layout)(s["a"], s["sfa"], s["b"], s["sfb"], s["c"], s["d"])
         elif self.kind == "DenseFP4":
@@ -266,7 +279,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10,11", help="comma-separated 1-based workload indices")
+    ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10,11,12,13", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")
