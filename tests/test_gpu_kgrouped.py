@@ -111,3 +111,13 @@ def test_kgrouped_rejects(dg):
         dg.dg_k_grouped_fp8_gemm_tn_contiguous(dev(q.a), dev(q.sfa), dev(q.b), dev(q.sfb), None,
                                                torch.zeros((1, 40, 48), dtype=torch.float32, device="cuda"), [128])
     assert e.value.status == -2
+
+
+def test_kgrouped_rejects_too_many_groups(dg):
+    log("case: k-grouped with 257 groups (the limit is 256)")
+    p = inputgen.exact_kgrouped(1, 32, 48, [128], seed=5)
+    d = torch.zeros((257, 32, 48), dtype=torch.float32, device="cuda")
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_k_grouped_fp8_gemm_tn_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), None, d,
+                                               [128] + [0] * 256)
+    assert e.value.status == -2

@@ -541,3 +541,18 @@ def test_dense_long_k_wide_n_decode_shape(dg):
     got = run_dense(dg, p)
     rows = np.array([0, 1, 31, 32, 63])
     check_tolerance(got[rows], oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c, rows=rows), "64x16000x16384")
+
+
+def test_dense_rejects_too_wide_n(dg):
+    # N = 2**22: the tile kernels' column offsets would leave 32 bits; real
+    # buffers of that shape, so nothing is out of bounds even if it launched
+    log("case: dense 1 x 4194304 x 128 is rejected")
+    N = 1 << 22
+    a = torch.zeros((1, 128), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((N, 128), dtype=torch.uint8, device="cuda")
+    sfa = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    sfb = torch.ones((N // 128, 1), dtype=torch.float32, device="cuda")
+    d = torch.zeros((1, N), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_fp8_gemm_nt(a, sfa, b, sfb, None, d)
+    assert e.value.status == -2
