@@ -659,8 +659,11 @@ fp8_gemm_nt_kernel(PT p) {
     // one K block from slot u (compile-time): fragments, promotion factors, MFMAs.
     // The loads of block `next` into slot next_u are spread between the MFMAs so
     // the vector-memory queue drains while the matrix cores run.
-    auto compute = [&](auto u_const, int next, int next_u, float live) {
+    // sma_const: the A strips computed (all of them, or the first half when
+    // the wave's valid rows fit in them)
+    auto compute = [&](auto u_const, int next, int next_u, float live, auto sma_const) {
       constexpr int u = decltype(u_const)::value;
+      constexpr int SMA = decltype(sma_const)::value;
       // the block's B scale (K-grouped: 1, the per-column scales enter below)
       const float sb = (KG || B4) ? live : lds_f32(offSB + u * S::S_BYTES) * live;
       auto frag = [&](uint32_t lo_addr, uint32_t hi_addr) {
@@ -680,8 +683,9 @@ fp8_gemm_nt_kernel(PT p) {
         if constexpr (TB) return kmajor_frag<BN>(offB0[j & 1] + j * 128 + u * S::B_BYTES);
         else return frag(offB0[0] + j * 2048 + u * S::B_BYTES, offB0[1] + j * 2048 + u * S::B_BYTES);
       };
-      constexpr int T = S::SM * S::SN;
+      constexpr int T = SMA * S::SN;
       constexpr int STRIDE = T / S::LPS > 0 ? T / S::LPS : 1;
+      static_assert(!E8M0 || SMA == S::SM, "the MFMA-scaled path computes every strip");
       if constexpr (E8M0) {
         // scale exponents: the biased fp32 exponent of 2^e is its E8M0 code;
         // lane l scales A row l%16 of the strip and B column l%16.  All A strips
@@ -736,7 +740,7 @@ fp8_gemm_nt_kernel(PT p) {
 #pragma unroll
       for (int t = 0; t < T + P - 1; ++t) {
         if (t < T) {
-          if (t % S::SN == 0 && t / S::SN + 1 < S::SM) {
+          if (t % S::SN == 0 && t / S::SN + 1 < SMA) {
             // keep the scheduler from hoisting every strip's reads to the top
             if constexpr (S::SM * S::SN >= 32) __builtin_amdgcn_sched_barrier(0);
             load_strip(t / S::SN + 1);
@@ -761,6 +765,12 @@ fp8_gemm_nt_kernel(PT p) {
           a.z = __builtin_fmaf(q.z, c.z, a.z);
           a.w = __builtin_fmaf(q.w, c.w, a.w);
         }
+      }
+      // with fewer MFMAs than loads (half the strips of a small wave tile) the
+      // rest of the next block's loads follow the MFMAs
+      if constexpr (T < S::LPS) {
+#pragma unroll
+        for (int k = T; k < S::LPS; ++k) issue_one(k, next, next_u);
       }
       // nothing of the next block is hoisted into this one (bounds live fragments)
       __builtin_amdgcn_sched_barrier(0);
@@ -802,7 +812,8 @@ fp8_gemm_nt_kernel(PT p) {
           if (i < kbs) {
             wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
             bare_barrier();
-            compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, 1.f);
+            compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, 1.f,
+                    std::integral_constant<int, S::SM>{});
           }
         });
       }
@@ -812,14 +823,25 @@ fp8_gemm_nt_kernel(PT p) {
       // its slot) and promotes it with a zero factor.  Every step is then the
       // same straight-line code, which keeps the VGPR accumulators in place.
       const int steps = (kbs + NSLOT - 1) / NSLOT * NSLOT;
-      for (int i0 = 0; i0 < steps; i0 += NSLOT) {
-        static_for<NSLOT>([&](auto u_const) {
-          constexpr int u = decltype(u_const)::value;
-          const int i = i0 + u;
-          wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
-          bare_barrier();
-          compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, i < kbs ? 1.f : 0.f);
-        });
+      auto run = [&](auto sma_const) {
+        for (int i0 = 0; i0 < steps; i0 += NSLOT) {
+          static_for<NSLOT>([&](auto u_const) {
+            constexpr int u = decltype(u_const)::value;
+            const int i = i0 + u;
+            wait_vm_lgkm0<(NSLOT - 2) * S::LPS>();
+            bare_barrier();
+            compute(u_const, min(i + NSLOT - 1, kbs - 1), (u + NSLOT - 1) % NSLOT, i < kbs ? 1.f : 0.f, sma_const);
+          });
+        }
+      };
+      // masked groups: a wave whose valid rows fit in its first half of strips
+      // computes only those (its other strips' results are never stored)
+      if constexpr (MODE == kMasked && S::SM % 2 == 0) {
+        const bool half = __builtin_amdgcn_readfirstlane(rows_lim - (m0 + wrow0) <= S::WTM / 2 ? 1 : 0) != 0;
+        if (half) run(std::integral_constant<int, S::SM / 2>{});
+        else run(std::integral_constant<int, S::SM>{});
+      } else {
+        run(std::integral_constant<int, S::SM>{});
       }
     }
 
