@@ -4,13 +4,19 @@
 // Configuration choice (the pages' host heuristics pick a kernel layout and
 // launch shape per problem; prefill and decode shapes get different kernels,
 // zwt0204 DeepGEMM deep dive, "它的核心思路" point 2):
-//   * dense shapes with at most 64 rows take the narrow kernel (16x48 tiles
+//   * dense NT shapes with at most 16 rows take the narrow kernel (16x48 tiles
 //     over the whole K, one launch) when its tiles occupy at least half the
-//     CUs, else the 64x64 decode tile with K split across workgroups followed
-//     by a split-K reduction kernel;
+//     CUs;
+//   * dense shapes (any operand storage, FP8 or FP4 B) with fewer 128x128
+//     tiles than half the CUs take the 64x64 decode tile with K split across
+//     workgroups (one split up to 8 K blocks, else enough splits of 4 to 8
+//     blocks to fill the chip) and a split-K reduction kernel, as long as the
+//     splits fit in about two rounds of the chip and in the workspace;
 //   * otherwise the fp32-promotion tile kernel with the largest tile that
-//     still gives every CU a tile (256x256, 128x256, else 128x128 with two
-//     workgroups per CU);
+//     still gives every CU a tile (256x256, 128x256, else 128x128 with a
+//     four-slot ring), 128-row tiles for contiguous calls, 128x256 rather
+//     than 256x256 when the call has a C; a last partial round of items is
+//     split over K where the tile allows (the split tail);
 //   * the power-of-two kernels (scales applied inside the MFMA) are selected
 //     with DG_FORCE_CONFIG; they run behind a scale check that leaves its
 //     verdicts on the device, beside the general kernel, and exactly one of

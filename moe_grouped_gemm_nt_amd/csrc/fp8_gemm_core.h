@@ -1,5 +1,6 @@
-// gfx950 kernels for the FP8 (e4m3) block-scaled GEMM, NT layout, and its two
-// M-grouped MoE forms.
+// gfx950 kernels for the FP8 (e4m3) block-scaled GEMM, NT layout, its two
+// M-grouped MoE forms, the other operand storages (nn, tn, tt), the K-grouped
+// TN form and FP8 x FP4.
 //
 // Computation (likun.im DeepGEMM article, section 一: D = C + A @ B in the NT
 // layout; aitangshan.cn DeepGEMM article, "4. FP8 精度优化的核心": each block's
@@ -11,9 +12,10 @@
 //
 // Two kernels share that per-block step:
 //
-// fp8_gemm_nt_kernel (prefill shapes and both grouped forms)
-//   * a workgroup of four waves owns a BM x BN output tile; each wave owns a
-//     (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in VGPRs;
+// fp8_gemm_nt_kernel (prefill shapes, both M-grouped forms, the K-grouped form)
+//   * a workgroup of WAVES_M x WAVES_N waves (four or eight) owns a BM x BN
+//     output tile; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held
+//     in VGPRs;
 //   * A and B K-blocks travel HBM -> LDS through the direct global->LDS path
 //     (global_load_lds_dwordx4: no VGPR staging) into a ring of NSLOT slots,
 //     so up to NSLOT-1 K-blocks are in flight while one feeds the MFMAs; each
@@ -23,13 +25,19 @@
 //   * workgroups walk a list of work items; the list is split into 8
 //     contiguous ranges, one per XCD (the hardware deals workgroups to the
 //     XCDs round-robin), so that tiles sharing A rows or B columns run on the
-//     same XCD and meet in its L2;
+//     same XCD and meet in its L2; the items of a last, partial round may be
+//     split over K (the split tail: fp32 partials that a reduction kernel
+//     sums);
 //   * masked form: each workgroup builds the per-group tile counts from the
 //     device-resident masked_m in LDS and walks the expert groups, skipping
 //     empty ones; contiguous form: the expert of each 128-row block is read
-//     from the device-resident grouped_layout.
+//     from the device-resident grouped_layout; waves with no valid rows skip
+//     their MFMAs;
+//   * template bits select K-major ("t" / second "n") operands, an FP4 (E2M1)
+//     B with E8M0 scales applied by the MFMA, MFMA-applied power-of-two
+//     scales, and the K-grouped form (per-column B scales, fp32 D).
 //
-// fp8_gemm_nt_decode_kernel (dense shapes with few rows)
+// fp8_gemm_nt_decode_kernel (dense shapes with few rows; fp8_gemm.hip)
 //   * a workgroup owns a 64x64 tile and a range of at most 8 K-blocks (a K
 //     split); its four waves split those K-blocks among themselves, each wave
 //     loading and consuming only its own blocks with no barrier in the K loop;
@@ -40,11 +48,6 @@
 //     split stores its fp32 partial to a workspace and splitk_reduce_kernel,
 //     launched next on the same stream, sums the splits in split order
 //     (deterministic), adds C and rounds; the kernel boundary orders the two.
-//     An in-kernel alternative (selected on the host) lets the last split to
-//     arrive do that sum: partials go through device-scope (sc1) stores and
-//     loads, coherent across the XCDs' L2 caches without flushing or
-//     invalidating them, and a per-tile arrival counter is reset to zero by
-//     the last split for the next call.
 //
 // LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row so that the
 // fragment reads of a 16-row strip are free of bank conflicts.
