@@ -150,3 +150,34 @@ def test_fp4_masked_exact(dg, monkeypatch, cfg):
     ref, written = oracle.m_grouped_fp8_fp4_masked(a, sfa, b, sfb, masked_m)
     assert np.array_equal(got[written], ref[written])
     assert np.all(got[~written] == 0xDEAD)
+
+
+@pytest.mark.parametrize("cfg", ["1", "0", "6"])
+def test_fp4_in_place_c_equals_d(dg, monkeypatch, cfg):
+    log(f"case: fp8 x fp4 in place (c == d), forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = inputgen.exact_dense_fp4(200, 464, 1024, seed=23)
+    cd = bf16_bits_dev(p.c)
+    dg.dg_fp8_fp4_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), cd, cd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(cd), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+def test_fp4_masked_with_c(dg):
+    # masked FP8 x FP4 with a bf16 C [G][max_m][N]
+    log("case: fp8 x fp4 masked with C")
+    G, max_m, N, K = 3, 160, 272, 512
+    base = inputgen.exact_dense_fp4(G * max_m, N, K, seed=24)
+    a = base.a.reshape(G, max_m, K)
+    sfa = np.ascontiguousarray(base.sfa.reshape(K // 128, G, max_m).transpose(1, 0, 2))
+    c = base.c.reshape(G, max_m, N)
+    b, sfb = _fp4_experts(G, N, K, 50)
+    masked_m = np.array([160, 3, 77], dtype=np.int32)
+    d = sentinel_like((G, max_m, N))
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(dev(a), dev(sfa), dev(b), dev(sfb), bf16_bits_dev(c), d,
+                                           dev(masked_m), 64)
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_fp8_fp4_masked(a, sfa, b, sfb, masked_m, c)
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == 0xDEAD)

@@ -141,3 +141,16 @@ def test_layout_decode_kernel_exact(dg, monkeypatch, layout, splits, M, N, K):
     p = inputgen.exact_dense(M, N, K, seed=M + K)
     got, a, b = run_layout(dg, layout, p)
     assert np.array_equal(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("cfg", ["1", "0", "11"])
+def test_layout_in_place_c_equals_d(dg, monkeypatch, layout, cfg):
+    log(f"case: {layout} in place (c == d), forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    p = inputgen.exact_dense(192, 336, 1024, seed=19)
+    a, b = stored(layout, p)
+    cd = bf16_bits_dev(p.c)
+    getattr(dg, CALLS[layout])(dev(a), dev(p.sfa), dev(b), dev(p.sfb), cd, cd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(cd), oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c))

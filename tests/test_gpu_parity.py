@@ -556,3 +556,18 @@ def test_dense_rejects_too_wide_n(dg):
     with pytest.raises(dg.DGError) as e:
         dg.dg_fp8_gemm_nt(a, sfa, b, sfb, None, d)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("cfg", ["1", "0", "6", "11"])
+def test_dense_in_place_every_path(dg, monkeypatch, cfg):
+    # c == d through the decode kernel (one split writes D itself; several go
+    # through the reduction), the tile kernels that read C a strip ahead of
+    # their stores (0, 6) and the one that reads it per element (11), and the
+    # split tail
+    log(f"case: in-place c == d, forced config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    for M, N, K in [(96, 200, 512), (300, 2112, 1024)]:
+        p = inputgen.exact_dense(M, N, K, seed=M + 1)
+        cd = bf16_bits_dev(p.c)
+        got = run_dense(dg, p, c_dev=cd, out=cd)
+        assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)), (M, N, K)
