@@ -220,9 +220,12 @@ class Workload:
                                                s["masked_m"], self.p.expected_m)
 
 
-def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool = True):
+def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool = True, repeats=None):
     """Runs `warmup` untimed steps, then times exactly `steps` steps between a
-    synchronisation on each side.  Returns (total ms, per-step ms)."""
+    synchronisation on each side.  Returns (total ms, per-step ms).  With
+    `repeats` (a list), the captured graph is then replayed that many more
+    times, each replay timed on its own, and the per-step times are appended
+    (outside the timed region, for the median and minimum)."""
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
@@ -249,6 +252,16 @@ def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool =
         end.record(stream)
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
+    if repeats is not None and graph is not None:
+        for _ in range(10):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                graph.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            repeats.append(e0.elapsed_time(e1) / steps)
     return total, total / steps
 
 
@@ -312,7 +325,8 @@ def main():
         steps = args.steps
         if w.flops > 1e11:
             steps = max(10, min(steps, 50))         # large shapes: keep the timed region short
-        total_ms, ms = time_workload(torch, w, steps, args.warmup, use_graph=not args.no_graph)
+        reps = [] if idx == HEADLINE else None
+        total_ms, ms = time_workload(torch, w, steps, args.warmup, use_graph=not args.no_graph, repeats=reps)
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.bytes / (ms * 1e-3) / 1e9
         rec = {"ms_per_call": round(ms, 5), "tflops": round(tflops, 2),
@@ -325,6 +339,9 @@ def main():
             f"of FP8 peak), {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
         if idx == HEADLINE:
             head = (w, steps, total_ms, ms, tflops, gbs)
+            if reps:
+                rec["repeat_ms_per_call"] = {"replays": len(reps), "median": round(float(np.median(reps)), 6),
+                                             "min": round(float(np.min(reps)), 6)}
         else:
             del w
             torch.cuda.empty_cache()
