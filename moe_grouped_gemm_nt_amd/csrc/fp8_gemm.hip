@@ -20,7 +20,6 @@ constexpr int DNW = 4;                            // waves per workgroup
 // for an FP4 B, its packed E8M0 column scales
 template <bool B4> constexpr int dslot() { return DBM * KBLK + DBN * (B4 ? KBLK / 2 : KBLK) + DBM * 4 + (B4 ? DBN * 4 : 0); }
 template <bool B4> constexpr int dlpb() { return DBM / 8 + DBN / (B4 ? 16 : 8) + 1 + B4; }   // loads per K block (one wave)
-constexpr int DSLOT = dslot<false>();
 constexpr int DLPB = dlpb<false>();
 constexpr int DNPW = DKBS / DNW;                  // K blocks per wave
 constexpr int DT = (DBM / 16) * (DBN / 16);       // 16x16 sub-tiles of the tile

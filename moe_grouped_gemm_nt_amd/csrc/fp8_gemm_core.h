@@ -116,6 +116,10 @@ __device__ __forceinline__ void wait_stages(int n) {
 // read as dependent on every load in flight (it cannot tell the ring slots
 // apart and would wait for all of them); the kernels wait on vmcnt themselves.
 // One wait state separates the M0 write from the load that uses it.
+// (The asm writes M0 and lists it as clobbered; the compiler notes that M0 is a
+// reserved register, which is expected here.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
@@ -124,6 +128,7 @@ __device__ __forceinline__ void dma_4(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   // the C-style cast is an address-space cast: generic -> LDS offset
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)(p));
@@ -322,10 +327,13 @@ __device__ __forceinline__ float lds_f32(uint32_t addr) {
 
 // Direct global->LDS load with a uniform 64-bit base in SGPRs and a 32-bit
 // per-lane byte offset.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // E8M0 = false: MFMA partials promoted by fp32 FMAs (any scales).
 // E8M0 = true:  every scale is a power of two, applied by the MFMA itself from
