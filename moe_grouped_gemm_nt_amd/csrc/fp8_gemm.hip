@@ -1,7 +1,10 @@
-// gfx950 kernels for the FP8 block-scaled GEMM, NT layout: instantiations of
-// the tile kernel with fp32 promotion on the VALU (any fp32 scales), the
-// decode kernel and its split-K reduction, and the launch dispatch.  The
-// kernels themselves are described in fp8_gemm_core.h.
+// gfx950 kernels for the FP8 block-scaled GEMM: instantiations of the tile
+// kernel with fp32 promotion on the VALU (any fp32 scales) for every form
+// (dense in the four storages, M-grouped contiguous and masked, K-grouped,
+// FP8 x FP4), the decode kernel (64x64 tiles with K split over workgroups, in
+// any operand storage and with an FP4 B) and its split-K reduction, the
+// narrow kernel, the split-tail reduction, and the launch dispatch.  The tile
+// and decode kernels' structure is described in fp8_gemm_core.h.
 //
 // Built with MFMA results in VGPRs (-amdgpu-mfma-vgpr-form), where the
 // promotion FMAs read them.

@@ -340,7 +340,10 @@ __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32
 //               its E8M0 exponent; results accumulate in place (AGPRs).
 // LAYOUT: bit 0 set = A is stored K-major ([K][M], M contiguous: the "t" of
 //         "tn"/"tt"), bit 1 set = B is stored [K][N] (the second "n" of
-//         "nn"/"tn"); clear bits are the K-contiguous "nt" operands.
+//         "nn"/"tn"); clear bits are the K-contiguous "nt" operands; bit 2
+//         (LAYOUT 4) = B holds packed FP4 (E2M1) codes, 64 bytes per row per K
+//         block, with E8M0 scales per column per 32 K values that the MFMA
+//         applies (sfb int32 [K/128][N], four scale bytes per int).
 // MODE kKGrouped (PT = KGroupedParams): work items are (group, tile) pairs;
 // group g's K range is k_start[g] .. k_start[g+1]-1, both operands K-major,
 // B scales per column, fp32 D and C.
