@@ -160,10 +160,14 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
     // CU, three blocks in flight).  Contiguous calls stay at 128-row tiles: a
     // 256-row tile that spans two experts' segments runs once per expert, and
     // on the measured expert mixes that costs more than the larger tile saves.
-    const long long m_rows = (long long)rows * (mode == dg::kMasked ? groups : 1);
-    const long long tiles256 = ((m_rows + 255) / 256) * ((N + 255) / 256);
-    const long long tiles128x256 = ((m_rows + 127) / 128) * ((N + 255) / 256);
-    if (mode != dg::kContiguous && tiles256 >= num_cus) ch.cfg = dg::kCfg256x256w8;
+    // Masked calls: every group rounds up to its own m-tiles, and groups
+    // expected to hold fewer than 128 rows keep 128-row tiles (measured on
+    // 32 groups of 4-64 rows: 128x256 tiles 4-5% faster than the others).
+    const bool masked = mode == dg::kMasked;
+    const long long g = masked ? groups : 1;
+    const long long tiles256 = g * (((long long)rows + 255) / 256) * ((N + 255) / 256);
+    const long long tiles128x256 = g * (((long long)rows + 127) / 128) * ((N + 255) / 256);
+    if (mode != dg::kContiguous && !(masked && rows < 128) && tiles256 >= num_cus) ch.cfg = dg::kCfg256x256w8;
     else if (tiles128x256 >= num_cus) ch.cfg = dg::kCfg128x256w8;
     else ch.cfg = dg::kCfg128x128;
   }
