@@ -153,22 +153,21 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
     if (KB > 8 && fill > splits) splits = fill < cap ? fill : cap;
     ch.splits = splits;
   } else {
-    // the largest tile that still gives every CU a tile: per K block a CU
-    // loads (BM+BN)*128 bytes for BM*BN/256 MFMAs, and the loads bound these
-    // kernels, so bigger tiles run faster once the chip is full.  With fewer
-    // tiles than CUs, 128x128 tiles with the deepest ring (one workgroup per
-    // CU, three blocks in flight).  Contiguous calls stay at 128-row tiles: a
-    // 256-row tile that spans two experts' segments runs once per expert, and
-    // on the measured expert mixes that costs more than the larger tile saves.
-    // Masked calls: every group rounds up to its own m-tiles, and groups
+    // Tile kernels: per K block a CU loads (BM+BN)*128 bytes for BM*BN/256
+    // MFMAs, and the loads bound these kernels, so bigger tiles run faster.
+    // Contiguous calls stay at 128-row tiles: a 256-row tile that spans two
+    // experts' segments runs once per expert, and on the measured expert
+    // mixes that costs more than the larger tile saves.  Masked calls take the
+    // largest tile that still gives every CU a tile (128x128 below that, with
+    // the deepest ring): every group rounds up to its own m-tiles, and groups
     // expected to hold fewer than 128 rows keep 128-row tiles (measured on
     // 32 groups of 4-64 rows: 128x256 tiles 4-5% faster than the others).
     const bool masked = mode == dg::kMasked;
     const long long g = masked ? groups : 1;
     const long long tiles256 = g * (((long long)rows + 255) / 256) * ((N + 255) / 256);
     const long long tiles128x256 = g * (((long long)rows + 127) / 128) * ((N + 255) / 256);
-    if (mode == dg::kDense) {
-      // Dense: the tiles are bound by the bytes each CU loads per K block,
+    if (mode == dg::kDense || mode == dg::kContiguous) {
+      // Dense and contiguous: the tiles are bound by the bytes each CU loads per K block,
       // BM+BN rows of 128 bytes, so a call costs about its rounds of the chip
       // times that; a partial round of large tiles beats more rounds of small
       // ones (measured on 256-2048 x 2112-7168 x 7168: within 5% of the best
@@ -176,7 +175,8 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
       const long long tiles128 = (((long long)rows + 127) / 128) * ((N + 127) / 128);
       auto cost = [&](long long tiles, int edge) { return ((tiles + num_cus - 1) / num_cus) * edge; };
       const long long c256 = cost(tiles256, 512), c128x256 = cost(tiles128x256, 384), c128 = cost(tiles128, 256);
-      if (c256 <= c128x256 && c256 <= c128) ch.cfg = dg::kCfg256x256w8;
+      // (contiguous calls keep 128-row tiles: see above)
+      if (mode == dg::kDense && c256 <= c128x256 && c256 <= c128) ch.cfg = dg::kCfg256x256w8;
       else if (c128x256 <= c128) ch.cfg = dg::kCfg128x256w8;
       else ch.cfg = dg::kCfg128x128;
     } else if (mode != dg::kContiguous && !(masked && rows < 128) && tiles256 >= num_cus) {
