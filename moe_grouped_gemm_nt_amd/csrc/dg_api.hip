@@ -288,8 +288,8 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   if (s != DG_OK) return s;
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
   Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout);
-  // With a C the 128x256 tile is preferred: it reads C into its accumulators
-  // before the K loop, while the 256x256 tile must read it between its stores.
+  // With a C the 128x256 tile is preferred: it reads C a strip ahead of its
+  // stores, while the 256x256 tile must read it per element between them.
   if (ch.cfg == dg::kCfg256x256w8 && p.c && env_int("DG_FORCE_CONFIG", -1) < 0) ch.cfg = dg::kCfg128x256w8;
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
@@ -459,14 +459,17 @@ extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* s
   p.K = (int)K;
   p.G = num_groups;
   p.splits = 1;
-  // the largest tile that still gives every CU a work item (as for dense calls)
+  // the tile by rounds of the chip times the rows loaded per K block, as for
+  // dense calls; with a C the 256x256 tile is left out: it reads C per element
+  // between its stores, while the smaller tiles read it a strip ahead
   const long long t256 = (long long)num_groups * ((M + 255) / 256) * ((N + 255) / 256);
   const long long t128x256 = (long long)num_groups * ((M + 127) / 128) * ((N + 255) / 256);
-  // With a C the 128x256 tile is preferred: it reads C into its accumulators
-  // before the K loop, while the 256x256 tile must read it between its stores.
-  int cfg = t256 >= st->num_cus && !c ? dg::kCfg256x256w8
-            : t128x256 >= st->num_cus ? dg::kCfg128x256w8
-                                      : dg::kCfg128x128;
+  const long long t128 = (long long)num_groups * ((M + 127) / 128) * ((N + 127) / 128);
+  auto cost = [&](long long tiles, int edge) { return ((tiles + st->num_cus - 1) / st->num_cus) * edge; };
+  const long long c256 = cost(t256, 512), c128x256 = cost(t128x256, 384), c128 = cost(t128, 256);
+  int cfg = !c && c256 <= c128x256 && c256 <= c128 ? dg::kCfg256x256w8
+            : c128x256 <= c128                    ? dg::kCfg128x256w8
+                                                  : dg::kCfg128x128;
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 || forced == dg::kCfg256x256w8) cfg = forced;
   const dg::ConfigInfo& ci = dg::config_info(cfg);
