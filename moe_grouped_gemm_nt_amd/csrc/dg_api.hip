@@ -12,9 +12,11 @@
 //     workgroups (one split up to 8 K blocks, else enough splits of 4 to 8
 //     blocks to fill the chip) and a split-K reduction kernel, as long as the
 //     splits fit in about two rounds of the chip and in the workspace;
-//   * otherwise the fp32-promotion tile kernel with the largest tile that
-//     still gives every CU a tile (256x256, 128x256, else 128x128 with a
-//     four-slot ring), 128-row tiles for contiguous calls, 128x256 rather
+//   * otherwise the fp32-promotion tile kernel: dense, contiguous and
+//     K-grouped calls take the tile (256x256, 128x256 or 128x128) that
+//     minimises the rounds of the chip times the rows loaded per K block
+//     (128-row tiles for contiguous calls); masked calls the largest tile that
+//     still gives every CU one, counting m-tiles per group; 128x256 rather
 //     than 256x256 when the call has a C; a last partial round of items is
 //     split over K where the tile allows (the split tail);
 //   * the power-of-two kernels (scales applied inside the MFMA) are selected
