@@ -6,7 +6,7 @@
 // zwt0204 DeepGEMM deep dive, "它的核心思路" point 2):
 //   * dense NT shapes with at most 16 rows take the narrow kernel (16x48 tiles
 //     over the whole K, one launch) when its tiles occupy at least half the
-//     CUs;
+//     CUs or K is at most 16 blocks;
 //   * dense shapes (any operand storage, FP8 or FP4 B) with fewer 128x128
 //     tiles than half the CUs take the 64x64 decode tile with K split across
 //     workgroups (one split up to 8 K blocks, else enough splits of 4 to 8
@@ -134,9 +134,11 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
   const bool kmajor = ab_layout != 0;
   const int KB = K / 128;
   const long long tiles128 = (long long)((rows + 127) / 128) * ((N + 127) / 128);
-  if (!kmajor && mode == dg::kDense && rows <= 16 && KB > 0 && (N + 47) / 48 >= num_cus / 2) {
-    // one 16-row strip and enough 16x48 tiles to occupy half the chip:
-    // whole-K tiles, one launch, nothing crosses workgroups
+  if (!kmajor && mode == dg::kDense && rows <= 16 && KB > 0 && ((N + 47) / 48 >= num_cus / 2 || KB <= 16)) {
+    // one 16-row strip and enough 16x48 tiles to occupy half the chip, or a
+    // K short enough that one launch beats a split and its reduction (1 or 16
+    // rows, N 2112, K 2048: 4.4-4.9 us against 7.2-7.5): whole-K tiles, one
+    // launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
   } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus &&
              decode_fits(((long long)(rows + 63) / 64) * ((N + 63) / 64), KB, num_cus)) {
