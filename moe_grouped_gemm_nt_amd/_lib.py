@@ -87,9 +87,17 @@ def _check(fn: str, status: int):
 
 _CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 _BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8,)
 
 
-def _ptr(t, name, dtypes, allow_none=False):
+def _ptr(t, name, dtypes, shape, allow_none=False):
+    """The address of t after checking its dtype, shape and layout: the
+    library sees pointers and sizes only, so a tensor of another
+    shape would be read or written out of bounds by the kernels.  shape None
+    skips the shape check (scales when K is not a multiple of 128, which the
+    library rejects itself)."""
     if t is None:
         if allow_none:
             return None
@@ -98,11 +106,35 @@ def _ptr(t, name, dtypes, allow_none=False):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
     return t.data_ptr()
+
+
+def _on_device(**tensors):
+    """Every tensor must live on the current device: the library runs the
+    call there (checked after all shapes, so shape errors name the tensor
+    even for host tensors)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device.index is not None and t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name} is on {t.device}; the call runs on the current device "
+                             f"cuda:{torch.cuda.current_device()}")
+
+
+def _kb(K):
+    """K blocks of 128, or None when K is not a multiple of 128 (rejected by the library)."""
+    return K // 128 if K % 128 == 0 else None
+
+
+def _sh(*dims):
+    """A shape, or None when one of its sizes is unknown."""
+    return None if any(x is None for x in dims) else dims
 
 
 def _stream(stream):
@@ -121,42 +153,44 @@ def dg_version() -> int:
     return load().dg_version()
 
 
+def _dense(fn, a, sfa, b, sfb, c, d, M, N, K, a_shape, b_shape, stream):
+    """The dense calls (every operand storage): scales sfa [K/128][M] and
+    sfb [ceil(N/128)][K/128], c and d [M][N]."""
+    kb, nb = _kb(K), (N + 127) // 128
+    args = (_ptr(a, "a", _CODE_DTYPES, a_shape), _ptr(sfa, "sfa", _F32, _sh(kb, M)),
+            _ptr(b, "b", _CODE_DTYPES, b_shape), _ptr(sfb, "sfb", _F32, _sh(nb, kb)),
+            _ptr(c, "c", _BF16_DTYPES, (M, N), True), _ptr(d, "d", _BF16_DTYPES, (M, N)),
+            M, N, K)
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d)
+    _check(fn, getattr(load(), fn)(*args, _stream(stream)))
+
+
 def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
     """d[M][N] = bf16(c + a[M][K] . b[N][K]^T) with sfa [K/128][M], sfb [ceil(N/128)][K/128]."""
     M, K = a.shape
     N = b.shape[0]
-    _check("dg_fp8_gemm_nt", load().dg_fp8_gemm_nt(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
-
-
-def _dense_layout(fn, a, sfa, b, sfb, c, d, M, N, K, stream):
-    _check(fn, getattr(load(), fn)(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
+    _dense("dg_fp8_gemm_nt", a, sfa, b, sfb, c, d, M, N, K, (M, K), (N, K), stream)
 
 
 def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d, stream=None) -> None:
     """d[M][N] = bf16(c + a[M][K] . b[K][N]) (B stored K-major), scales as in the NT call."""
     M, K = a.shape
     N = b.shape[1]
-    _dense_layout("dg_fp8_gemm_nn", a, sfa, b, sfb, c, d, M, N, K, stream)
+    _dense("dg_fp8_gemm_nn", a, sfa, b, sfb, c, d, M, N, K, (M, K), (K, N), stream)
 
 
 def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d, stream=None) -> None:
     """d[M][N] = bf16(c + a[K][M]^T . b[K][N]) (both operands stored K-major)."""
     K, M = a.shape
     N = b.shape[1]
-    _dense_layout("dg_fp8_gemm_tn", a, sfa, b, sfb, c, d, M, N, K, stream)
+    _dense("dg_fp8_gemm_tn", a, sfa, b, sfb, c, d, M, N, K, (K, M), (K, N), stream)
 
 
 def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d, stream=None) -> None:
     """d[M][N] = bf16(c + a[K][M]^T . b[N][K]^T) (A stored K-major)."""
     K, M = a.shape
     N = b.shape[0]
-    _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, M, N, K, stream)
+    _dense("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, M, N, K, (K, M), (N, K), stream)
 
 
 def dg_fp8_fp4_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
@@ -164,65 +198,84 @@ def dg_fp8_fp4_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
     (four E8M0 exponents per int, one per 32 K values)."""
     M, K = a.shape
     N = b.shape[0]
-    _check("dg_fp8_fp4_gemm_nt", load().dg_fp8_fp4_gemm_nt(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, _stream(stream)))
+    kb = _kb(K)
+    args = (_ptr(a, "a", _CODE_DTYPES, (M, K)), _ptr(sfa, "sfa", _F32, _sh(kb, M)),
+            _ptr(b, "b", _U8, (N, K // 2)), _ptr(sfb, "sfb", _I32, _sh(kb, N)),
+            _ptr(c, "c", _BF16_DTYPES, (M, N), True), _ptr(d, "d", _BF16_DTYPES, (M, N)),
+            M, N, K)
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d)
+    _check("dg_fp8_fp4_gemm_nt", load().dg_fp8_fp4_gemm_nt(*args, _stream(stream)))
 
 
 def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:
-    """Contiguous M-grouped form: a [M][K], b [G][N][K], grouped_layout int32 [M]."""
+    """Contiguous M-grouped form: a [M][K], b [G][N][K], sfa [K/128][M],
+    sfb [G][ceil(N/128)][K/128], grouped_layout int32 [M]."""
     M, K = a.shape
     G, N, _ = b.shape
-    _check("dg_m_grouped_fp8_gemm_nt_contiguous", load().dg_m_grouped_fp8_gemm_nt_contiguous(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, G,
-        _ptr(grouped_layout, "grouped_layout", (torch.int32,)), _stream(stream)))
+    kb = _kb(K)
+    args = (_ptr(a, "a", _CODE_DTYPES, (M, K)), _ptr(sfa, "sfa", _F32, _sh(kb, M)),
+            _ptr(b, "b", _CODE_DTYPES, (G, N, K)), _ptr(sfb, "sfb", _F32, _sh(G, (N + 127) // 128, kb)),
+            _ptr(c, "c", _BF16_DTYPES, (M, N), True), _ptr(d, "d", _BF16_DTYPES, (M, N)), M, N, K, G,
+            _ptr(grouped_layout, "grouped_layout", _I32, (M,)))
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d, grouped_layout=grouped_layout)
+    _check("dg_m_grouped_fp8_gemm_nt_contiguous", load().dg_m_grouped_fp8_gemm_nt_contiguous(*args, _stream(stream)))
 
 
 def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, c, d, masked_m, expected_m, stream=None) -> None:
-    """Masked M-grouped form: a [G][max_m][K], b [G][N][K], masked_m int32 [G] on the device."""
+    """Masked M-grouped form: a [G][max_m][K], b [G][N][K], sfa [G][K/128][max_m],
+    sfb [G][ceil(N/128)][K/128], masked_m int32 [G] on the device."""
     G, max_m, K = a.shape
     N = b.shape[1]
-    _check("dg_m_grouped_fp8_gemm_nt_masked", load().dg_m_grouped_fp8_gemm_nt_masked(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), max_m, N, K, G,
-        _ptr(masked_m, "masked_m", (torch.int32,)), int(expected_m), _stream(stream)))
+    kb = _kb(K)
+    args = (_ptr(a, "a", _CODE_DTYPES, (G, max_m, K)), _ptr(sfa, "sfa", _F32, _sh(G, kb, max_m)),
+            _ptr(b, "b", _CODE_DTYPES, (G, N, K)), _ptr(sfb, "sfb", _F32, _sh(G, (N + 127) // 128, kb)),
+            _ptr(c, "c", _BF16_DTYPES, (G, max_m, N), True), _ptr(d, "d", _BF16_DTYPES, (G, max_m, N)),
+            max_m, N, K, G, _ptr(masked_m, "masked_m", _I32, (G,)), int(expected_m))
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d, masked_m=masked_m)
+    _check("dg_m_grouped_fp8_gemm_nt_masked", load().dg_m_grouped_fp8_gemm_nt_masked(*args, _stream(stream)))
 
 
 def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, c, d, ks, stream=None) -> None:
     """K-grouped TN form: a [K][M], b [K][N], sfa [K/128][M], sfb [K/128][N], c and d fp32
-    [G][M][N]; ks is a host sequence of per-group K sizes (multiples of 128)."""
+    [G][M][N]; ks is a host sequence of per-group K sizes (multiples of 128) summing to K."""
     K, M = a.shape
     N = b.shape[1]
-    ks_host = (ctypes.c_int32 * len(ks))(*[int(k) for k in ks])
-    _check("dg_k_grouped_fp8_gemm_tn_contiguous", load().dg_k_grouped_fp8_gemm_tn_contiguous(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", _CODE_DTYPES), _ptr(sfb, "sfb", (torch.float32,)),
-        _ptr(c, "c", (torch.float32,), True), _ptr(d, "d", (torch.float32,)), M, N, len(ks),
-        ctypes.cast(ks_host, ctypes.c_void_p), _stream(stream)))
+    ks = [int(k) for k in ks]
+    # sizes that are negative or not multiples of 128 are the library's to reject
+    if all(k >= 0 and k % 128 == 0 for k in ks) and sum(ks) != K:
+        raise ValueError(f"the group sizes sum to {sum(ks)}; a has K = {K} rows")
+    G = len(ks)
+    kb = _kb(K)
+    ks_host = (ctypes.c_int32 * G)(*ks)
+    args = (_ptr(a, "a", _CODE_DTYPES, (K, M)), _ptr(sfa, "sfa", _F32, _sh(kb, M)),
+            _ptr(b, "b", _CODE_DTYPES, (K, N)), _ptr(sfb, "sfb", _F32, _sh(kb, N)),
+            _ptr(c, "c", _F32, (G, M, N), True), _ptr(d, "d", _F32, (G, M, N)), M, N, G,
+            ctypes.cast(ks_host, ctypes.c_void_p))
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d)
+    _check("dg_k_grouped_fp8_gemm_tn_contiguous", load().dg_k_grouped_fp8_gemm_tn_contiguous(*args, _stream(stream)))
 
 
 def dg_m_grouped_fp8_fp4_gemm_nt_contiguous(a, sfa, b, sfb, c, d, grouped_layout, stream=None) -> None:
     """Contiguous M-grouped FP8 x FP4 form: a [M][K], b packed [G][N][K/2], sfb int32 [G][K/128][N]."""
     M, K = a.shape
     G, N, _ = b.shape
-    _check("dg_m_grouped_fp8_fp4_gemm_nt_contiguous", load().dg_m_grouped_fp8_fp4_gemm_nt_contiguous(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), M, N, K, G,
-        _ptr(grouped_layout, "grouped_layout", (torch.int32,)), _stream(stream)))
+    kb = _kb(K)
+    args = (_ptr(a, "a", _CODE_DTYPES, (M, K)), _ptr(sfa, "sfa", _F32, _sh(kb, M)),
+            _ptr(b, "b", _U8, (G, N, K // 2)), _ptr(sfb, "sfb", _I32, _sh(G, kb, N)),
+            _ptr(c, "c", _BF16_DTYPES, (M, N), True), _ptr(d, "d", _BF16_DTYPES, (M, N)), M, N, K, G,
+            _ptr(grouped_layout, "grouped_layout", _I32, (M,)))
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d, grouped_layout=grouped_layout)
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_contiguous", load().dg_m_grouped_fp8_fp4_gemm_nt_contiguous(*args, _stream(stream)))
 
 
 def dg_m_grouped_fp8_fp4_gemm_nt_masked(a, sfa, b, sfb, c, d, masked_m, expected_m, stream=None) -> None:
     """Masked M-grouped FP8 x FP4 form: a [G][max_m][K], b packed [G][N][K/2], sfb int32 [G][K/128][N]."""
     G, max_m, K = a.shape
     N = b.shape[1]
-    _check("dg_m_grouped_fp8_fp4_gemm_nt_masked", load().dg_m_grouped_fp8_fp4_gemm_nt_masked(
-        _ptr(a, "a", _CODE_DTYPES), _ptr(sfa, "sfa", (torch.float32,)),
-        _ptr(b, "b", (torch.uint8,)), _ptr(sfb, "sfb", (torch.int32,)),
-        _ptr(c, "c", _BF16_DTYPES, True), _ptr(d, "d", _BF16_DTYPES), max_m, N, K, G,
-        _ptr(masked_m, "masked_m", (torch.int32,)), int(expected_m), _stream(stream)))
-
+    kb = _kb(K)
+    args = (_ptr(a, "a", _CODE_DTYPES, (G, max_m, K)), _ptr(sfa, "sfa", _F32, _sh(G, kb, max_m)),
+            _ptr(b, "b", _U8, (G, N, K // 2)), _ptr(sfb, "sfb", _I32, _sh(G, kb, N)),
+            _ptr(c, "c", _BF16_DTYPES, (G, max_m, N), True), _ptr(d, "d", _BF16_DTYPES, (G, max_m, N)),
+            max_m, N, K, G, _ptr(masked_m, "masked_m", _I32, (G,)), int(expected_m))
+    _on_device(a=a, sfa=sfa, b=b, sfb=sfb, c=c, d=d, masked_m=masked_m)
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_masked", load().dg_m_grouped_fp8_fp4_gemm_nt_masked(*args, _stream(stream)))

@@ -102,3 +102,42 @@ def test_no_oracle_in_product_package():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "inputgen" not in src, f
+
+
+def test_python_binding_checks_shapes():
+    # the library sees pointers and sizes only, so the binding checks every
+    # tensor's shape against the sizes it passes (before the device check:
+    # host tensors reach the shape check)
+    import torch
+    u8 = torch.uint8
+    a, b = torch.zeros(64, 256, dtype=u8), torch.zeros(300, 256, dtype=u8)
+    d = torch.zeros(64, 300, dtype=torch.bfloat16)
+    sfa, sfb = torch.ones(2, 64), torch.ones(3, 2)
+    bad = {
+        "sfa": (a, torch.ones(64, 2), b, sfb, None, d),          # [M][K/128] instead of [K/128][M]
+        "sfb": (a, sfa, b, torch.ones(2, 3), None, d),
+        "d": (a, sfa, b, sfb, None, torch.zeros(300, 64, dtype=torch.bfloat16)),
+        "c": (a, sfa, b, sfb, torch.zeros(64, 299, dtype=torch.bfloat16), d),
+    }
+    for name, args in bad.items():
+        with pytest.raises(ValueError, match=f"^{name} has shape"):
+            dgpkg.dg_fp8_gemm_nt(*args)
+    with pytest.raises(ValueError, match="device tensor"):
+        dgpkg.dg_fp8_gemm_nt(a, sfa, b, sfb, None, d)           # shapes right, host memory
+    with pytest.raises(ValueError, match="^b has shape"):      # nn: B stored [K][N]
+        dgpkg.dg_fp8_gemm_nn(a, sfa, torch.zeros(255, 300, dtype=u8), sfb, None, d)
+    ga = torch.zeros(4, 32, 256, dtype=u8)
+    gb = torch.zeros(4, 300, 256, dtype=u8)
+    with pytest.raises(ValueError, match="^sfa has shape"):   # masked A scales [G][K/128][max_m]
+        dgpkg.dg_m_grouped_fp8_gemm_nt_masked(ga, torch.ones(2, 4, 32), gb, torch.ones(4, 3, 2), None,
+                                              torch.zeros(4, 32, 300, dtype=torch.bfloat16),
+                                              torch.zeros(4, dtype=torch.int32), 16)
+    with pytest.raises(ValueError, match="^grouped_layout has shape"):
+        dgpkg.dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, gb, torch.ones(4, 3, 2), None, d,
+                                                  torch.zeros(63, dtype=torch.int32))
+    with pytest.raises(ValueError, match="^b has shape"):      # FP4: two codes per byte
+        dgpkg.dg_fp8_fp4_gemm_nt(a, sfa, b, torch.zeros(2, 300, dtype=torch.int32), None, d)
+    ka, kbm = torch.zeros(384, 64, dtype=u8), torch.zeros(384, 48, dtype=u8)
+    with pytest.raises(ValueError, match="sum to 256"):
+        dgpkg.dg_k_grouped_fp8_gemm_tn_contiguous(ka, torch.ones(3, 64), kbm, torch.ones(3, 48), None,
+                                                  torch.zeros(2, 64, 48), [128, 128])
