@@ -6,7 +6,7 @@ fp32 sum the kernels form is exact in any order).
 The cases are drawn once from a fixed seed, so a failure names a case that
 reruns identically.  Shapes are ragged (M and N not multiples of the tiles,
 1 row, 1 column where the storage allows it) and K runs from one K block to
-24.  Forced configurations that do not apply to a call are ignored by the
+24 (K-grouped: groups of 0 to 9 K blocks, fp32 C and D).  Forced configurations that do not apply to a call are ignored by the
 library (it then chooses by itself), so every drawn combination is valid."""
 import numpy as np
 import pytest
@@ -19,18 +19,18 @@ from tests.gpu_util import SENTINEL, bf16_bits_dev, bits_host, dev, sentinel_lik
 pytestmark = pytest.mark.gpu
 
 FORMS = ["nt"] * 12 + ["nn", "tn", "tt"] * 3 + ["fp4"] * 7 + ["contiguous"] * 7 + ["masked"] * 7 + \
-        ["fp4_contiguous"] * 3 + ["fp4_masked"] * 3
+        ["fp4_contiguous"] * 3 + ["fp4_masked"] * 3 + ["kgrouped"] * 5
 CALLS = {"nt": "dg_fp8_gemm_nt", "nn": "dg_fp8_gemm_nn", "tn": "dg_fp8_gemm_tn", "tt": "dg_fp8_gemm_tt"}
 
 
-def draw_cases(n=64, seed=2026):
+def draw_cases(n=160, seed=2026):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
         form = str(rng.choice(FORMS))
         K = 128 * int(rng.integers(1, 25))
-        a_kmajor = form in ("tn", "tt")
-        b_kmajor = form in ("nn", "tn")
+        a_kmajor = form in ("tn", "tt", "kgrouped")
+        b_kmajor = form in ("nn", "tn", "kgrouped")
         M = int(rng.choice([1, 16, 64, 100, 128, 250, 333, 512, 700]))
         M = max(16, M // 16 * 16) if a_kmajor else M
         N = int(rng.choice([1, 48, 130, 256, 400, 777, 1100, 2112]))
@@ -59,6 +59,8 @@ def draw_cases(n=64, seed=2026):
                 case["max_m"] = max_m
                 case["masked_m"] = [int(x) for x in rng.integers(0, max_m + 1, size=G)]
                 case["expected_m"] = int(rng.choice([1, 64, 128, 256]))
+        if form == "kgrouped":
+            case["ks"] = [128 * int(x) for x in rng.choice([0, 1, 2, 5, 9], size=int(rng.integers(1, 6)))]
         cases.append(case)
     return cases
 
@@ -71,6 +73,8 @@ def case_id(c):
         shape = f"counts{'_'.join(map(str, c['counts']))}x{c['N']}x{c['K']}"
     elif "masked_m" in c:
         shape = f"G{c['G']}x{c['max_m']}x{c['N']}x{c['K']}-m{'_'.join(map(str, c['masked_m']))}"
+    elif "ks" in c:
+        shape = f"{c['M']}x{c['N']}-ks{'_'.join(map(str, c['ks']))}"
     else:
         shape = f"{c['M']}x{c['N']}x{c['K']}"
     return f"{c['i']}-{c['form']}-{shape}" + ("-c" if c["with_c"] else "") + \
@@ -158,12 +162,24 @@ def run_masked_case(dg, c):
     assert np.all(got[~written] == SENTINEL)
 
 
+def run_kgrouped_case(dg, c):
+    p = inputgen.exact_kgrouped(len(c["ks"]), c["M"], c["N"], c["ks"], seed=c["seed"], with_c=c["with_c"])
+    ref = oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c)
+    d = torch.full((p.G, p.M, p.N), -12345.5, dtype=torch.float32, device="cuda")
+    cc = dev(p.c) if p.c is not None else None
+    dg.dg_k_grouped_fp8_gemm_tn_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), cc, d, p.ks)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("case", CASES, ids=case_id)
 def test_random_case_exact(dg, monkeypatch, case):
     print(f"case: {case_id(case)}", flush=True)
     for k, v in case["env"].items():
         monkeypatch.setenv(k, v)
-    if "contiguous" in case["form"]:
+    if case["form"] == "kgrouped":
+        run_kgrouped_case(dg, case)
+    elif "contiguous" in case["form"]:
         run_contiguous_case(dg, case)
     elif "masked" in case["form"]:
         run_masked_case(dg, case)
