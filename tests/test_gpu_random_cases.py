@@ -7,14 +7,20 @@ The cases are drawn once from a fixed seed, so a failure names a case that
 reruns identically.  Shapes are ragged (M and N not multiples of the tiles,
 1 row, 1 column where the storage allows it) and K runs from one K block to
 24 (K-grouped: groups of 0 to 9 K blocks, fp32 C and D).  Forced configurations that do not apply to a call are ignored by the
-library (it then chooses by itself), so every drawn combination is valid."""
+library (it then chooses by itself), so every drawn combination is valid.
+
+A second set of cases draws random data (A ~ N(0,1), B ~ N(0,0.02), C ~
+N(0,0.1), scales amax/448 not rounded to powers of two, so the general
+promotion path runs) and checks the bf16 bound |d - ref| <= 8e-3 |ref| +
+1e-3 rms(ref) with a relative Frobenius error <= 2e-3 (K-grouped: the fp32
+accumulation bound of the K-grouped tests)."""
 import numpy as np
 import pytest
 import torch
 
 import inputgen
 import oracle
-from tests.gpu_util import SENTINEL, bf16_bits_dev, bits_host, dev, sentinel_like
+from tests.gpu_util import SENTINEL, bf16_bits_dev, bits_host, check_tolerance, dev, sentinel_like
 
 pytestmark = pytest.mark.gpu
 
@@ -185,3 +191,73 @@ def test_random_case_exact(dg, monkeypatch, case):
         run_masked_case(dg, case)
     else:
         run_dense_case(dg, case)
+
+
+RANDOM_FORMS = ("nt", "nn", "tn", "tt", "fp4", "contiguous", "masked", "kgrouped")
+RANDOM_CASES = [c for c in draw_cases(n=96, seed=2027) if c["form"] in RANDOM_FORMS][:56]
+
+
+def run_random_case(dg, c):
+    M, N, K, form, seed = c["M"], c["N"], c["K"], c["form"], c["seed"]
+    c_std = 0.1 if c["with_c"] else None
+    if form == "fp4":
+        p = inputgen.make_dense_fp4(M, N, K, seed, 1.0, 0.02, c_std, False)
+        d = sentinel_like((M, N))
+        dg.dg_fp8_fp4_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb),
+                              bf16_bits_dev(p.c) if p.c is not None else None, d)
+        torch.cuda.synchronize()
+        check_tolerance(bits_host(d), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c), form)
+    elif form in CALLS:
+        p = inputgen.make_dense(M, N, K, seed, 1.0, 0.02, c_std, False)
+        a = p.a if form[0] == "n" else np.ascontiguousarray(p.a.T)
+        b = p.b if form[1] == "t" else np.ascontiguousarray(p.b.T)
+        d = sentinel_like((M, N))
+        getattr(dg, CALLS[form])(dev(a), dev(p.sfa), dev(b), dev(p.sfb),
+                                 bf16_bits_dev(p.c) if p.c is not None else None, d)
+        torch.cuda.synchronize()
+        check_tolerance(bits_host(d), oracle.gemm_layout(form, a, p.sfa, b, p.sfb, p.c), form)
+    elif form == "contiguous":
+        p = inputgen.make_contiguous(c["G"], N, K, max(1, sum(c["counts"])), seed, pow2=False,
+                                     with_c=c["with_c"], pad_id=-1)
+        d = sentinel_like((p.M, N))
+        dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb),
+                                               bf16_bits_dev(p.c) if p.c is not None else None, d,
+                                               dev(p.grouped_layout))
+        torch.cuda.synchronize()
+        got = bits_host(d)
+        ref, written = oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.grouped_layout, p.c)
+        check_tolerance(got[written], ref[written], form)
+        assert np.all(got[~written] == SENTINEL)
+    elif form == "masked":
+        p = inputgen.make_masked(c["G"], c["max_m"], N, K, seed, c["expected_m"], pow2=False,
+                                 with_c=c["with_c"], masked_m=c["masked_m"])
+        d = sentinel_like((p.G, p.max_m, N))
+        dg.dg_m_grouped_fp8_gemm_nt_masked(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb),
+                                           bf16_bits_dev(p.c) if p.c is not None else None, d,
+                                           dev(p.masked_m), p.expected_m)
+        torch.cuda.synchronize()
+        got = bits_host(d)
+        ref, written = oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m, p.c)
+        if written.any():
+            check_tolerance(got[written], ref[written], form)
+        assert np.all(got[~written] == SENTINEL)
+    else:
+        p = inputgen.make_kgrouped(len(c["ks"]), M, N, max(1, sum(c["ks"])), seed, pow2=False,
+                                   with_c=c["with_c"])
+        d = torch.full((p.G, p.M, p.N), -12345.5, dtype=torch.float32, device="cuda")
+        dg.dg_k_grouped_fp8_gemm_tn_contiguous(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb),
+                                               dev(p.c) if p.c is not None else None, d, p.ks)
+        torch.cuda.synchronize()
+        got = d.cpu().numpy().astype(np.float64)
+        acc, mag = oracle.k_grouped_tn_acc(p.a, p.sfa, p.b, p.sfb, p.ks, p.c)
+        kb = (np.asarray(p.ks) // 128).astype(np.float64)[:, None, None]
+        bound = 2.0 ** -24 * (2 * 128 + kb + 4) * mag + 1e-30
+        assert np.all(np.isfinite(got)) and np.all(np.abs(got - acc) <= bound)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=case_id)
+def test_random_case_tolerance(dg, monkeypatch, case):
+    print(f"case: random data {case_id(case)}", flush=True)
+    for k, v in case["env"].items():
+        monkeypatch.setenv(k, v)
+    run_random_case(dg, case)
