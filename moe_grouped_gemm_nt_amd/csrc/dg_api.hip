@@ -125,6 +125,24 @@ bool decode_fits(long long tiles64, int KB, int num_cus) {
   return wgs <= 2LL * num_cus + num_cus / 4 && wgs * 64 * 64 * (long long)sizeof(float) <= (long long)kWorkspaceBytes;
 }
 
+// Estimated time (µs) of a call whose tiles all fit in one round of the chip,
+// with the split tail of plan_split_tail: each CU loads (BM+BN) rows of 128
+// bytes for each of its KB/sk K blocks at the per-CU rate the tile kernels
+// measure (about 35 GB/s with the split tail, 40 GB/s without, when some CUs
+// stay idle), and the sk fp32 partial tiles are written and read back at
+// about 5 TB/s.
+double split_tail_us(long long tiles, int bm, int bn, int KB, int num_cus) {
+  const long long slots = num_cus / 8;
+  const long long tail = (tiles + 7) / 8;        // items of the fullest XCD
+  long long sk = tail > 0 ? slots / tail : 1;
+  sk = std::min<long long>({sk, 16, (long long)KB});
+  while (sk > 1 && 8 * tail * sk * bm * bn * (long long)sizeof(float) > (long long)kWorkspaceBytes) --sk;
+  if (sk < 2) sk = 1;
+  const double load = (double)KB / (double)sk * (bm + bn) * 128.0 / (sk > 1 ? 35e3 : 40e3);
+  const double partials = sk > 1 ? 2.0 * (double)sk * tiles * bm * bn * sizeof(float) / 5e6 : 0.0;
+  return load + partials;
+}
+
 // rows: rows computed per group (dense: M; contiguous: M; masked: expected rows per group)
 // ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn); 4 an FP4 B.  The
 // other layouts are read by the 128x128, 128x256 and 256x256 tile kernels and
@@ -181,6 +199,17 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
       const long long c256 = cost(tiles256, 512), c128x256 = cost(tiles128x256, 384), c128 = cost(tiles128, 256);
       // (contiguous calls keep 128-row tiles: see above)
       if (mode == dg::kDense && c256 <= c128x256 && c256 <= c128) ch.cfg = dg::kCfg256x256w8;
+      else if (tiles128 <= num_cus && KB > 0)
+        // one round either way: the split tail divides K over the idle CUs,
+        // so the larger tile's fewer bytes per output count against its larger
+        // partials.  The larger tile is taken only when the estimate gives it
+        // a 5% margin: closer than that the measured order went either way,
+        // while beyond it the larger tile measured faster (128x256 against
+        // 128x128: 1024x2112x7168 38.7 against 43.0 us, 384x4096x16384 46.7
+        // against 54.3, 512x4096x16384 57.3 against 59.2).
+        ch.cfg = split_tail_us(tiles128x256, 128, 256, KB, num_cus) <
+                         0.95 * split_tail_us(tiles128, 128, 128, KB, num_cus)
+                     ? dg::kCfg128x256w8 : dg::kCfg128x128;
       else if (c128x256 <= c128) ch.cfg = dg::kCfg128x256w8;
       else ch.cfg = dg::kCfg128x128;
     } else if (mode != dg::kContiguous && !(masked && rows < 128) && tiles256 >= num_cus) {
