@@ -15,7 +15,9 @@
 //   * otherwise the fp32-promotion tile kernel: dense, contiguous and
 //     K-grouped calls take the tile (256x256, 128x256 or 128x128) that
 //     minimises the rounds of the chip times the rows loaded per K block
-//     (128-row tiles for contiguous calls); masked calls the largest tile that
+//     (128-row tiles for contiguous calls), and where 128x128 and 128x256
+//     both fit in one round, an estimate of the split tail's loads and fp32
+//     partials decides between them; masked calls the largest tile that
 //     still gives every CU one, counting m-tiles per group; 128x256 rather
 //     than 256x256 when the call has a C; a last partial round of items is
 //     split over K where the tile allows (the split tail);
