@@ -176,6 +176,24 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* sfa, const v
                                         const float* sfb, const float* c, float* d, int M, int N,
                                         int num_groups, const int32_t* ks, void* stream);
 
+/* The kernel configuration the calls above would choose, as a host-side query
+ * that touches no device (for tests and for callers that want to know what
+ * runs).  form: 0 dense (any operand storage), 1 contiguous, 2 masked.  rows:
+ * M for dense and contiguous calls, expected_m for masked ones.  ab_layout:
+ * 0 nt, 1 tt (A stored [K][M]), 2 nn (B stored [K][N]), 3 tn, 4 FP4 B.
+ * num_cus: the device's compute units (256 on MI355X).  has_c: nonzero when
+ * the call passes a C.  Writes the configuration id to *cfg (0 128x128 tile,
+ * 1 decode kernel with K split over workgroups, 2 128x64, 3 64x128, 4 128x128
+ * two per CU, 5 256x128, 6 128x256, 7 and 8 128x256 and 10 256x256 with
+ * power-of-two scales in the MFMA, 9 narrow 16x48 whole-K, 11 256x256) and
+ * the decode kernel's K splits to *splits (1 otherwise).  DG_FORCE_CONFIG and
+ * DG_FORCE_SPLITS act as they do on the calls.  Returns DG_ERR_INVALID_ARG
+ * for NULL outputs, a form outside 0-2, rows or N below 1, K negative or not
+ * a multiple of 128, num_groups below 1, num_cus below 8 or ab_layout
+ * outside 0-4; DG_OK otherwise. */
+int dg_choose_config(int form, int rows, int N, int K, int num_groups, int num_cus, int ab_layout,
+                     int has_c, int* cfg, int* splits);
+
 /* Prepares per-device state for the current HIP device (device properties and
  * the split-K workspace, allocated once and kept until the process ends).
  * Calls above do this lazily on first use; call dg_init() first when the

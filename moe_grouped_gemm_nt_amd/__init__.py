@@ -6,6 +6,7 @@ from ._lib import (  # noqa: F401
     DGError,
     EXPORTED,
     LIB_PATH,
+    dg_choose_config,
     dg_fp8_fp4_gemm_nt,
     dg_fp8_gemm_nn,
     dg_fp8_gemm_nt,

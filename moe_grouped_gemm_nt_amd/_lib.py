@@ -30,6 +30,7 @@ EXPORTED = [
     "dg_m_grouped_fp8_fp4_gemm_nt_contiguous",
     "dg_m_grouped_fp8_fp4_gemm_nt_masked",
     "dg_k_grouped_fp8_gemm_tn_contiguous",
+    "dg_choose_config",
     "dg_init",
     "dg_last_error",
     "dg_version",
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dg_m_grouped_fp8_fp4_gemm_nt_masked.restype = ci
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp, vp]
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = ci
+        lib.dg_choose_config.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+        lib.dg_choose_config.restype = ci
         lib.dg_init.argtypes = []
         lib.dg_init.restype = ci
         lib.dg_last_error.argtypes = []
@@ -147,6 +150,20 @@ def _stream(stream):
 
 def dg_init() -> None:
     _check("dg_init", load().dg_init())
+
+
+FORMS = {"dense": 0, "contiguous": 1, "masked": 2}
+AB_LAYOUTS = {"nt": 0, "tt": 1, "nn": 2, "tn": 3, "fp4": 4}
+
+
+def dg_choose_config(form, rows, N, K, num_groups=1, num_cus=256, ab_layout="nt", has_c=False):
+    """(configuration id, decode K splits) the calls would choose; host-only,
+    touches no device.  rows is M, or expected_m for the masked form."""
+    cfg, splits = ctypes.c_int(-1), ctypes.c_int(0)
+    _check("dg_choose_config", load().dg_choose_config(
+        FORMS[form], int(rows), int(N), int(K), int(num_groups), int(num_cus), AB_LAYOUTS[ab_layout],
+        1 if has_c else 0, ctypes.byref(cfg), ctypes.byref(splits)))
+    return cfg.value, splits.value
 
 
 def dg_version() -> int:

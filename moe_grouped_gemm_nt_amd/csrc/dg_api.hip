@@ -317,15 +317,21 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
   return grid;
 }
 
+// The choice for one call: choose(), then with a C the 128x256 tile in place
+// of the 256x256 one: it reads C a strip ahead of its stores, while the
+// 256x256 tile must read it per element between them.
+Choice choose_call(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout, bool has_c) {
+  Choice ch = choose(mode, rows, N, K, groups, num_cus, ab_layout);
+  if (ch.cfg == dg::kCfg256x256w8 && has_c && env_int("DG_FORCE_CONFIG", -1) < 0) ch.cfg = dg::kCfg128x256w8;
+  return ch;
+}
+
 int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   DeviceState* st = nullptr;
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
-  Choice ch = choose(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout);
-  // With a C the 128x256 tile is preferred: it reads C a strip ahead of its
-  // stores, while the 256x256 tile must read it per element between them.
-  if (ch.cfg == dg::kCfg256x256w8 && p.c && env_int("DG_FORCE_CONFIG", -1) < 0) ch.cfg = dg::kCfg128x256w8;
+  Choice ch = choose_call(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout, p.c != nullptr);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
@@ -604,6 +610,19 @@ extern "C" int dg_m_grouped_fp8_fp4_gemm_nt_masked(const void* a, const float* s
                                                    int expected_m, void* stream) {
   return grouped_masked(a, sfa, b, reinterpret_cast<const float*>(sfb), c, d, max_m, N, K, num_groups, masked_m,
                         expected_m, 4, stream);
+}
+
+extern "C" int dg_choose_config(int form, int rows, int N, int K, int num_groups, int num_cus, int ab_layout,
+                                int has_c, int* cfg, int* splits) {
+  if (!cfg || !splits) return fail(DG_ERR_INVALID_ARG, "cfg and splits must not be NULL");
+  if (form < dg::kDense || form > dg::kMasked) return fail(DG_ERR_INVALID_ARG, "form=%d is not 0, 1 or 2", form);
+  if (rows < 1 || N < 1 || K < 0 || K % 128 != 0 || num_groups < 1 || num_cus < 8 || ab_layout < 0 || ab_layout > 4)
+    return fail(DG_ERR_INVALID_ARG, "invalid query (rows=%d N=%d K=%d num_groups=%d num_cus=%d ab_layout=%d)", rows,
+                N, K, num_groups, num_cus, ab_layout);
+  const Choice ch = choose_call(form, rows, N, K, num_groups, num_cus, ab_layout, has_c != 0);
+  *cfg = ch.gated_cfg >= 0 ? ch.gated_cfg : ch.cfg;
+  *splits = ch.splits;
+  return DG_OK;
 }
 
 extern "C" int dg_init(void) {
