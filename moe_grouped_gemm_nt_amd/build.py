@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -54,12 +55,15 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, extra_flags=None) -> str:
     objdir = os.path.join(PKG_DIR, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs = []
     for src, flags in SOURCES.items():
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        _run([hipcc()] + HIPCC_FLAGS + flags + list(extra_flags or []) +
-             ["-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([hipcc()] + HIPCC_FLAGS + flags + list(extra_flags or []) +
+                     ["-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    # the sources compile independently; one process each
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [obj for _, obj in jobs]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)

@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -58,7 +59,7 @@ constexpr int kMaxDevices = 64;
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;    // split-K partial tiles
 
 struct DeviceState {
-  bool ready = false;
+  std::atomic<bool> ready{false};   // set once, with release order, after the fields below
   int num_cus = 0;
   float* workspace = nullptr;
   int32_t* verdicts = nullptr;    // scale check results, dg::kCheckWGs entries
@@ -73,20 +74,27 @@ int get_device_state(DeviceState** out) {
   if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index %d out of range", dev);
   DeviceState& st = g_dev[dev];
-  if (!st.ready) {
+  if (!st.ready.load(std::memory_order_acquire)) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (!st.ready) {
+    if (!st.ready.load(std::memory_order_relaxed)) {
       hipDeviceProp_t prop;
       e = hipGetDeviceProperties(&prop, dev);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
       if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(DG_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950 only", dev, prop.gcnArchName);
-      st.num_cus = prop.multiProcessorCount;
-      e = hipMalloc(&st.workspace, kWorkspaceBytes);
+      float* ws = nullptr;
+      int32_t* verdicts = nullptr;
+      e = hipMalloc(&ws, kWorkspaceBytes);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace): %s", hipGetErrorString(e));
-      e = hipMalloc(&st.verdicts, sizeof(int32_t) * dg::kCheckWGs);
-      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(verdicts): %s", hipGetErrorString(e));
-      st.ready = true;
+      e = hipMalloc(&verdicts, sizeof(int32_t) * dg::kCheckWGs);
+      if (e != hipSuccess) {
+        (void)hipFree(ws);   // nothing is kept from a failed set-up; the next call tries again
+        return fail(DG_ERR_HIP, "hipMalloc(verdicts): %s", hipGetErrorString(e));
+      }
+      st.num_cus = prop.multiProcessorCount;
+      st.workspace = ws;
+      st.verdicts = verdicts;
+      st.ready.store(true, std::memory_order_release);
     }
   }
   *out = &st;
@@ -227,8 +235,10 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   const bool forced_ok = !kmajor || forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 ||
                          forced == dg::kCfg256x256w8 || forced == dg::kCfgDecode;
+  // (the decode and narrow kernels are dense-only and need a K block: with
+  // K = 0 a forced choice of them is ignored)
   if (forced >= 0 && forced < dg::kNumConfigs && forced_ok &&
-      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || mode == dg::kDense)) {
+      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || (mode == dg::kDense && KB > 0))) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
       ch.cfg = dg::kCfg128x128x2;
       ch.gated_cfg = forced;

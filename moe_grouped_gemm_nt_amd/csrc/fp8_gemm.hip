@@ -159,7 +159,8 @@ fp8_gemm_nt_decode_kernel(Params p) {
   const int nown = kbs > wave ? (kbs - wave + DNW - 1) / DNW : 0;
   float sb[DNPW];                 // the block's B scale (FP4: 1, the MFMA applies the E8M0 scales)
 #pragma unroll
-  for (int j = 0; j < DNPW; ++j) sb[j] = B4 ? 1.f : p.sfb[(size_t)nb * KB + min(kb0 + wave + DNW * j, KB - 1)];
+  for (int j = 0; j < DNPW; ++j)
+    sb[j] = B4 || j >= nown ? 1.f : p.sfb[(size_t)nb * KB + kb0 + wave + DNW * j];   // only blocks the wave owns
 
   // issue every load of this wave's blocks: A (64 rows), B (64 rows), A scales
   const int lr = lane >> 3;

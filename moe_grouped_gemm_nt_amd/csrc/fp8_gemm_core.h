@@ -496,13 +496,18 @@ fp8_gemm_nt_kernel(PT p) {
         tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
       }
       if constexpr (MODE == kContiguous) {
-        // the expert of each 128-row block of the tile: the largest id among
-        // its rows (padding rows may carry -1); all valid ids in a block agree
+        // the expert of each 128-row block of the tile: the largest valid id
+        // among its rows; ids outside [0, G) (padding, conventionally -1) count
+        // as -1, so that they never hide the block's valid rows.  All valid ids
+        // in a block agree.
         if (wave < CBLK) {
           int best = -1;
           for (int r = lane; r < BM / CBLK; r += 64) {
             const int row = mt * BM + wave * (BM / CBLK) + r;
-            if (row < p.rows) best = max(best, p.layout[row]);
+            if (row < p.rows) {
+              const int id = p.layout[row];
+              best = max(best, id >= 0 && id < p.G ? id : -1);
+            }
           }
           for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
           if (lane == 0) s_group[wave] = best;

@@ -101,12 +101,16 @@ fp8_gemm_nt_ws_kernel(Params p) {
     } else {
       tile_coords(w, p.tiles_m, p.tiles_n, mt, nt);
       if constexpr (MODE == kContiguous) {
-        // every wave finds the block's expert itself (largest id among its
-        // rows; padding rows may carry -1), so no workgroup sync is needed
+        // every wave finds the block's expert itself (largest valid id among
+        // its rows; ids outside [0, G), conventionally -1 on padding rows,
+        // count as -1), so no workgroup sync is needed
         int best = -1;
         for (int r = lane; r < BM; r += 64) {
           const int row = mt * BM + r;
-          if (row < p.rows) best = max(best, p.layout[row]);
+          if (row < p.rows) {
+            const int id = p.layout[row];
+            best = max(best, id >= 0 && id < p.G ? id : -1);
+          }
         }
         for (int off = 32; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off));
         group = __builtin_amdgcn_readfirstlane(best);

@@ -70,3 +70,12 @@ def test_invalid_query(args):
     with pytest.raises(dg.DGError) as e:
         dg.dg_choose_config(*args)
     assert e.value.status == -1
+
+
+def test_forced_decode_or_narrow_ignored_without_k_blocks(monkeypatch):
+    # K = 0 gives D = C; the decode and narrow kernels index their first K
+    # block's scales, so a forced choice of them is ignored there
+    for forced in ("1", "9"):
+        monkeypatch.setenv("DG_FORCE_CONFIG", forced)
+        assert dg.dg_choose_config("dense", 64, 2112, 0)[0] not in (1, 9)
+        assert dg.dg_choose_config("dense", 64, 2112, 128)[0] == int(forced)

@@ -409,6 +409,42 @@ def test_contiguous_exact_with_padding_ids_and_empty_expert(dg, monkeypatch, cfg
     del rng
 
 
+@pytest.mark.parametrize("cfg,sk", [(None, "0"), (None, "4"), ("0", "0"), ("0", "4"), ("6", "4"), ("11", None),
+                                    ("7", None), ("8", None), ("10", None)])
+def test_contiguous_exact_out_of_range_padding_ids(dg, monkeypatch, cfg, sk):
+    # padding rows carry ids outside [0, G) other than -1 (G, G + 3, a large
+    # id): a block's valid rows must still be computed, and the padding rows
+    # left untouched, with the split tail on and off
+    log(f"case: contiguous exact, padding ids >= G, config {cfg}, split tail {sk}")
+    if cfg is not None:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    if sk is not None:
+        monkeypatch.setenv("DG_SK_SPLITS", sk)
+    G, N, K = 4, 200, 768
+    counts = np.array([130, 7, 256, 1])
+    segs = [((c + 127) // 128) * 128 for c in counts]
+    M = sum(segs)
+    pad_ids = np.array([G, G + 3, 1 << 20, -1], dtype=np.int32)
+    layout = np.empty(M, dtype=np.int32)
+    off = 0
+    for g, (cnt, sg) in enumerate(zip(counts, segs)):
+        layout[off:off + cnt] = g
+        layout[off + cnt:off + sg] = pad_ids[np.arange(sg - cnt) % len(pad_ids)]
+        off += sg
+    base = inputgen.exact_dense(M, N, K, seed=41)
+    b = np.stack([inputgen.exact_dense(1, N, K, seed=110 + g).b for g in range(G)])
+    sfb = np.stack([inputgen.exact_dense(1, N, K, seed=120 + g).sfb for g in range(G)])
+    d = sentinel_like((M, N))
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(dev(base.a), dev(base.sfa), dev(b), dev(sfb),
+                                           bf16_bits_dev(base.c), d, dev(layout))
+    torch.cuda.synchronize()
+    got = bits_host(d)
+    ref, written = oracle.m_grouped_contiguous(base.a, base.sfa, b, sfb, layout, base.c)
+    assert written.sum() == counts.sum()
+    assert np.array_equal(got[written], ref[written])
+    assert np.all(got[~written] == SENTINEL)
+
+
 @pytest.mark.slow
 def test_contiguous_config3_sampled(dg):
     log("case: contiguous config 3 (8 experts, 8192 rows, N=4096, K=7168) sampled rows")

@@ -395,6 +395,50 @@ def test_k_grouped_brute_force_tiny():
     assert not np.any(oracle.k_grouped_tn(a, sfa, b, sfb, ks)[1])
 
 
+def test_k_grouped_magnitude_brute_force():
+    # The second output of k_grouped_tn_acc (likun.im section 二, the
+    # k_grouped_fp8_gemm_tn_contiguous call with per-group K sizes) is the
+    # error scale of an fp32 accumulation: |C| plus the sum of the absolute
+    # values of every scaled product a*sa*b*sb of the group's K rows.  Exact
+    # rationals over the stored arrays, with mixed-sign codes (subnormals
+    # included), scales that are not powers of two (some negative, so that a
+    # dropped absolute value shows), an empty group and C; every value here
+    # has few significant bits, so the fp64 sums are exact and the two must
+    # agree exactly, for acc as well as for mag.
+    rng = np.random.default_rng(52)
+    G, M, N = 4, 3, 5
+    ks = np.array([256, 0, 128, 384], dtype=np.int32)
+    K = int(ks.sum())
+    a = _random_codes(rng, (K, M))
+    b = _random_codes(rng, (K, N))
+    a[0, 0], a[1, 0], b[0, 0] = 0x01, 0x85, 0x03        # subnormal codes of both signs
+    sfa = (rng.integers(1, 16, size=(K // 128, M)) * rng.choice([-1, 1], size=(K // 128, M)) / 8.0).astype(np.float32)
+    sfb = (rng.integers(1, 16, size=(K // 128, N)) / 4.0).astype(np.float32)
+    sfb[0, 1] = -0.75
+    c = rng.integers(-40, 41, size=(G, M, N)).astype(np.float32)
+    acc, mag = oracle.k_grouped_tn_acc(a, sfa, b, sfb, ks, c)
+    assert mag.shape == (G, M, N) and acc.shape == (G, M, N)
+    start = 0
+    for g in range(G):
+        for m in range(M):
+            for n in range(N):
+                tot = frac_f32(c[g, m, n])
+                mg = abs(frac_f32(c[g, m, n]))
+                for k in range(start, start + int(ks[g])):
+                    term = (frac_e4m3(int(a[k, m])) * frac_f32(sfa[k // 128, m])
+                            * frac_e4m3(int(b[k, n])) * frac_f32(sfb[k // 128, n]))
+                    tot += term
+                    mg += abs(term)
+                assert Fraction(float(acc[g, m, n])) == tot, (g, m, n)
+                assert Fraction(float(mag[g, m, n])) == mg, (g, m, n)
+        start += int(ks[g])
+    # the empty group: |C| only; without C, zero
+    assert np.array_equal(mag[1], np.abs(c[1]).astype(np.float64))
+    assert not np.any(oracle.k_grouped_tn_acc(a, sfa, b, sfb, ks)[1][1])
+    # a term-wise bound: mag dominates |acc| everywhere
+    assert np.all(mag >= np.abs(acc))
+
+
 def test_k_grouped_exact_regime_closed_form():
     # integer codes and power-of-two scales: Python integers (scaled by the
     # smallest scale product) give the exact value, which fp32 holds exactly
