@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="run only the microbenchmarks (MFMA loop, memory rates, launch cost) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -312,6 +314,10 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.ceilings:
+        from moe_grouped_gemm_nt_amd import ceilings
+        print(json.dumps({"ceilings": ceilings.measure(torch)}), flush=True)
         return
     dg.load()
     dg.dg_init()

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdg.so")
+CEILINGS_PATH = os.path.join(PKG_DIR, "libdg_ceilings.so")
 # source -> extra flags.  The fp32-promotion kernels want MFMA results in
 # VGPRs, where the promotion FMAs read them; the power-of-two-scale kernels
 # keep their accumulators in AGPRs.
@@ -67,7 +68,17 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
+    build_ceilings(verbose)
     return LIB_PATH
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """libdg_ceilings.so: the MFMA / memory / launch microbenchmarks (include/dg_ceilings.h)."""
+    tmp = CEILINGS_PATH + ".tmp"
+    _run([hipcc()] + HIPCC_FLAGS + ["-shared", "-I", INCLUDE, os.path.join(CSRC, "ceilings.hip"), "-o", tmp],
+         verbose)
+    os.replace(tmp, CEILINGS_PATH)
+    return CEILINGS_PATH
 
 
 if __name__ == "__main__":

@@ -141,3 +141,23 @@ def test_python_binding_checks_shapes():
     with pytest.raises(ValueError, match="sum to 256"):
         dgpkg.dg_k_grouped_fp8_gemm_tn_contiguous(ka, torch.ones(3, 64), kbm, torch.ones(3, 48), None,
                                                   torch.zeros(2, 64, 48), [128, 128])
+
+
+def test_ceilings_library_exports_every_declared_symbol():
+    # the microbenchmarks of include/dg_ceilings.h live in their own library
+    from moe_grouped_gemm_nt_amd import build, ceilings
+    if not os.path.exists(ceilings.CEILINGS_PATH):
+        build.build_ceilings()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dg_ceilings.h")).read(), flags=re.S)
+    syms = sorted(set(re.findall(r"\b(dgc_[a-z0-9_]+)\s*\(", text)))
+    assert syms == ["dgc_chase", "dgc_empty", "dgc_mfma", "dgc_stream"]
+    out = subprocess.run(["nm", "-D", "--defined-only", ceilings.CEILINGS_PATH], capture_output=True, text=True).stdout
+    assert set(syms) <= set(re.findall(r" T (dgc_[a-z0-9_]+)", out))
+    lib = ceilings.load()
+    # invalid arguments are refused on the host, before any HIP call
+    assert lib.dgc_stream(None, 4096, 1, 0, None, None) == -1
+    assert lib.dgc_stream(ctypes.c_void_p(0x1000), 1000, 1, 0, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.dgc_empty(0, None) == -1
+    assert lib.dgc_mfma(0, 1, 0, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.dgc_chase(ctypes.c_void_p(0x1000), 10, 3, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.dgc_chase(None, 10, 0, ctypes.c_void_p(0x1000), None) == -1
