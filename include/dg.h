@@ -176,6 +176,22 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* sfa, const v
                                         const float* sfb, const float* c, float* d, int M, int N,
                                         int num_groups, const int32_t* ks, void* stream);
 
+/* dg_fp8_gemm_nt without any device allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, arithmetic, layouts and
+ * errors as dg_fp8_gemm_nt.  Its kernels' scratch (split-K partial tiles and
+ * scale-check verdicts) is a fixed 8 MiB device array per GPU, part of the
+ * library's code object and held until the process ends; the call allocates
+ * nothing, neither on its first use on a device nor later.  The kernel
+ * configuration is chosen so that its partials fit the array; one forced
+ * beyond it (DG_FORCE_SPLITS) returns DG_ERR_UNSUPPORTED.  Every call on a GPU
+ * shares that GPU's array, and nothing in it needs clearing between calls
+ * (every call writes what it reads), but calls that may overlap on one GPU
+ * (different streams not ordered by events) race on it and must be ordered
+ * by the caller.  Returns a dg_status. */
+int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const float* sfb,
+                           const void* c, void* d, int M, int N, int K, void* stream);
+
 /* The kernel configuration the calls above would choose, as a host-side query
  * that touches no device (for tests and for callers that want to know what
  * runs).  form: 0 dense (any operand storage), 1 contiguous, 2 masked.  rows:

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     dg_fp8_fp4_gemm_nt,
     dg_fp8_gemm_nn,
     dg_fp8_gemm_nt,
+    dg_fp8_gemm_nt_noalloc,
     dg_fp8_gemm_tn,
     dg_fp8_gemm_tt,
     dg_init,

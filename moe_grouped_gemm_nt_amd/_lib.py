@@ -21,6 +21,7 @@ DG_ERR_HIP = -3
 
 EXPORTED = [
     "dg_fp8_gemm_nt",
+    "dg_fp8_gemm_nt_noalloc",
     "dg_fp8_gemm_nn",
     "dg_fp8_gemm_tn",
     "dg_fp8_gemm_tt",
@@ -56,7 +57,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             raise RuntimeError(f"{path} is missing: build it with `python -m moe_grouped_gemm_nt_amd.build`")
         lib = ctypes.CDLL(path)
         vp, fp, i32p, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
-        for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+        for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_noalloc", "dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
             getattr(lib, name).argtypes = [vp, fp, vp, fp, vp, vp, ci, ci, ci, vp]
             getattr(lib, name).restype = ci
         lib.dg_fp8_fp4_gemm_nt.argtypes = [vp, fp, vp, vp, vp, vp, ci, ci, ci, vp]
@@ -187,6 +188,14 @@ def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, stream=None) -> None:
     M, K = a.shape
     N = b.shape[0]
     _dense("dg_fp8_gemm_nt", a, sfa, b, sfb, c, d, M, N, K, (M, K), (N, K), stream)
+
+
+def dg_fp8_gemm_nt_noalloc(a, sfa, b, sfb, c, d, stream=None) -> None:
+    """As dg_fp8_gemm_nt, with the kernels' scratch in the library's fixed
+    per-device array: the call allocates no device memory."""
+    M, K = a.shape
+    N = b.shape[0]
+    _dense("dg_fp8_gemm_nt_noalloc", a, sfa, b, sfb, c, d, M, N, K, (M, K), (N, K), stream)
 
 
 def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d, stream=None) -> None:

@@ -130,9 +130,9 @@ int env_int(const char* name, int dflt) {
 // most 8 K blocks each) can need several rounds of the chip, and measured
 // beyond about two and a quarter rounds the tile kernels (with their split
 // tail) were faster.  Its fp32 partials must also fit the workspace.
-bool decode_fits(long long tiles64, int KB, int num_cus) {
+bool decode_fits(long long tiles64, int KB, int num_cus, size_t ws_bytes) {
   const long long wgs = tiles64 * ((KB + 7) / 8);
-  return wgs <= 2LL * num_cus + num_cus / 4 && wgs * 64 * 64 * (long long)sizeof(float) <= (long long)kWorkspaceBytes;
+  return wgs <= 2LL * num_cus + num_cus / 4 && wgs * 64 * 64 * (long long)sizeof(float) <= (long long)ws_bytes;
 }
 
 // Estimated time (µs) of a call whose tiles all fit in one round of the chip,
@@ -141,12 +141,12 @@ bool decode_fits(long long tiles64, int KB, int num_cus) {
 // measure (about 35 GB/s with the split tail, 40 GB/s without, when some CUs
 // stay idle), and the sk fp32 partial tiles are written and read back at
 // about 5 TB/s.
-double split_tail_us(long long tiles, int bm, int bn, int KB, int num_cus) {
+double split_tail_us(long long tiles, int bm, int bn, int KB, int num_cus, size_t ws_bytes) {
   const long long slots = num_cus / 8;
   const long long tail = (tiles + 7) / 8;        // items of the fullest XCD
   long long sk = tail > 0 ? slots / tail : 1;
   sk = std::min<long long>({sk, 16, (long long)KB});
-  while (sk > 1 && 8 * tail * sk * bm * bn * (long long)sizeof(float) > (long long)kWorkspaceBytes) --sk;
+  while (sk > 1 && 8 * tail * sk * bm * bn * (long long)sizeof(float) > (long long)ws_bytes) --sk;
   if (sk < 2) sk = 1;
   const double load = (double)KB / (double)sk * (bm + bn) * 128.0 / (sk > 1 ? 35e3 : 40e3);
   const double partials = sk > 1 ? 2.0 * (double)sk * tiles * bm * bn * sizeof(float) / 5e6 : 0.0;
@@ -157,7 +157,8 @@ double split_tail_us(long long tiles, int bm, int bn, int KB, int num_cus) {
 // ab_layout: 0 nt; 1-3 a K-major operand (tt, nn, tn); 4 an FP4 B.  The
 // other layouts are read by the 128x128, 128x256 and 256x256 tile kernels and
 // the decode kernel only.
-Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout) {
+// ws_bytes: the split-K workspace the call may use.
+Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout, size_t ws_bytes) {
   Choice ch{dg::kCfg128x128x2, 1, 0, -1};
   const bool kmajor = ab_layout != 0;
   const int KB = K / 128;
@@ -169,7 +170,7 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
     // launch, nothing crosses workgroups
     ch.cfg = dg::kCfgNarrow;
   } else if (mode == dg::kDense && KB > 0 && 2 * tiles128 < num_cus &&
-             decode_fits(((long long)(rows + 63) / 64) * ((N + 63) / 64), KB, num_cus)) {
+             decode_fits(((long long)(rows + 63) / 64) * ((N + 63) / 64), KB, num_cus, ws_bytes)) {
     // too few tiles to occupy half the chip (decode shapes): 64x64 tiles; split
     // K so that the workgroups fill the chip while each split keeps at most 8
     // K blocks, all of them in flight at once, and at least 4
@@ -217,8 +218,8 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
         // while beyond it the larger tile measured faster (128x256 against
         // 128x128: 1024x2112x7168 38.7 against 43.0 us, 384x4096x16384 46.7
         // against 54.3, 512x4096x16384 57.3 against 59.2).
-        ch.cfg = split_tail_us(tiles128x256, 128, 256, KB, num_cus) <
-                         0.95 * split_tail_us(tiles128, 128, 128, KB, num_cus)
+        ch.cfg = split_tail_us(tiles128x256, 128, 256, KB, num_cus, ws_bytes) <
+                         0.95 * split_tail_us(tiles128, 128, 128, KB, num_cus, ws_bytes)
                      ? dg::kCfg128x256w8 : dg::kCfg128x128;
       else if (c128x256 <= c128) ch.cfg = dg::kCfg128x256w8;
       else ch.cfg = dg::kCfg128x128;
@@ -265,13 +266,13 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
 // error).  The tile kernels walk their work list persistently: masked grids,
 // and both grids of a gated pair (one of which exits at once), hold only as
 // many workgroups as are resident on the chip together.
-int plan(int mode, int cfg, dg::Params& p, const DeviceState* st, bool gated) {
+int plan(int mode, int cfg, dg::Params& p, int num_cus, bool gated) {
   const dg::ConfigInfo& ci = dg::config_info(cfg);
   p.tiles_m = (p.rows + ci.bm - 1) / ci.bm;
   p.tiles_n = (p.N + ci.bn - 1) / ci.bn;
   long long items;
   // one workgroup per CU, except the two-workgroup 128x128 configuration
-  const long long resident = (long long)st->num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
+  const long long resident = (long long)num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
   if (mode == dg::kMasked) {
     items = (long long)p.G * p.tiles_m * p.tiles_n;     // upper bound; the kernel walks the real list
     if (items > resident) items = resident;
@@ -292,7 +293,7 @@ int plan(int mode, int cfg, dg::Params& p, const DeviceState* st, bool gated) {
 // tiles up to 128x256; the tile kernel writes fp32 partials that
 // splitk_tile_reduce_kernel sums).  Returns the grid (0 = no split tail) and
 // sets p.sk_splits / p.sk_tail.
-int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
+int plan_split_tail(int mode, int cfg, dg::Params& p, int num_cus, size_t ws_bytes) {
   const dg::ConfigInfo& ci = dg::config_info(cfg);
   p.sk_splits = 1;
   p.sk_tail = 0;
@@ -302,7 +303,7 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
       cfg == dg::kCfgE8_256x256)
     return 0;
   const int KB = p.K / 128;
-  const int resident = st->num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
+  const int resident = num_cus * (cfg == dg::kCfg128x128x2 ? 2 : 1);
   const int grid = resident / 8 * 8;
   const int slots = grid / 8;
   const long long total = (long long)p.tiles_m * p.tiles_n;
@@ -320,7 +321,7 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
   if (forced > 0) sk = forced;
   if (sk > KB) sk = KB;
   if (sk > 16) sk = 16;
-  while (sk > 1 && 8LL * tail * sk * ci.bm * ci.bn * (long long)sizeof(float) > (long long)kWorkspaceBytes) --sk;
+  while (sk > 1 && 8LL * tail * sk * ci.bm * ci.bn * (long long)sizeof(float) > (long long)ws_bytes) --sk;
   if (sk < 2) return 0;
   p.sk_splits = sk;
   p.sk_tail = tail;
@@ -330,51 +331,58 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, const DeviceState* st) {
 // The choice for one call: choose(), then with a C the 128x256 tile in place
 // of the 256x256 one: it reads C a strip ahead of its stores, while the
 // 256x256 tile must read it per element between them.
-Choice choose_call(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout, bool has_c) {
-  Choice ch = choose(mode, rows, N, K, groups, num_cus, ab_layout);
+Choice choose_call(int mode, int rows, int N, int K, int groups, int num_cus, int ab_layout, bool has_c,
+                   size_t ws_bytes) {
+  Choice ch = choose(mode, rows, N, K, groups, num_cus, ab_layout, ws_bytes);
   if (ch.cfg == dg::kCfg256x256w8 && has_c && env_int("DG_FORCE_CONFIG", -1) < 0) ch.cfg = dg::kCfg128x256w8;
   return ch;
 }
 
-int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
-  DeviceState* st = nullptr;
-  int s = get_device_state(&st);
-  if (s != DG_OK) return s;
+// What a call runs with: the device's compute units and the scratch memory
+// its kernels may use (split-K partials, scale-check verdicts).
+struct Resources {
+  int num_cus;
+  float* workspace;
+  size_t ws_bytes;
+  int32_t* verdicts;     // dg::kCheckWGs entries
+};
+
+int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, const Resources& r) {
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
-  Choice ch = choose_call(mode, rows_hint, p.N, p.K, p.G, st->num_cus, p.ab_layout, p.c != nullptr);
+  Choice ch = choose_call(mode, rows_hint, p.N, p.K, p.G, r.num_cus, p.ab_layout, p.c != nullptr, r.ws_bytes);
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
-  p.workspace = st->workspace;
-  p.workspace_bytes = kWorkspaceBytes;
+  p.workspace = r.workspace;
+  p.workspace_bytes = r.ws_bytes;
   p.gate_ok = nullptr;
-  int grid = plan(mode, ch.cfg, p, st, ch.gated_cfg >= 0);
+  int grid = plan(mode, ch.cfg, p, r.num_cus, ch.gated_cfg >= 0);
   if (grid == 0) return DG_ERR_UNSUPPORTED;
   p.sk_splits = 1;
   p.sk_tail = 0;
   if (ch.gated_cfg < 0 && ch.splits == 1) {
-    const int sk_grid = plan_split_tail(mode, ch.cfg, p, st);
+    const int sk_grid = plan_split_tail(mode, ch.cfg, p, r.num_cus, r.ws_bytes);
     if (sk_grid > 0) grid = sk_grid;
   }
   if (ch.splits > 1) {
     const long long need = (long long)p.tiles_m * p.tiles_n * ch.splits * ci.bm * ci.bn * (long long)sizeof(float);
-    if (need > (long long)kWorkspaceBytes)
-      return fail(DG_ERR_UNSUPPORTED, "split-K workspace of %lld bytes exceeds %zu", need, kWorkspaceBytes);
+    if (need > (long long)r.ws_bytes)
+      return fail(DG_ERR_UNSUPPORTED, "split-K workspace of %lld bytes exceeds the %zu available", need, r.ws_bytes);
   }
   hipError_t e = hipSuccess;
   if (ch.gated_cfg >= 0) {
     dg::Params pe = p;
-    const int grid_e = plan(mode, ch.gated_cfg, pe, st, true);
+    const int grid_e = plan(mode, ch.gated_cfg, pe, r.num_cus, true);
     if (grid_e == 0) return DG_ERR_UNSUPPORTED;
     const int KB = p.K / 128;
     const int NB = (p.N + 127) / 128;
     const size_t na = (size_t)KB * p.rows * (mode == dg::kMasked ? p.G : 1);
     const size_t nb = (size_t)NB * KB * (mode == dg::kDense ? 1 : p.G);
-    p.gate_ok = pe.gate_ok = st->verdicts;
+    p.gate_ok = pe.gate_ok = r.verdicts;
     if (env_int("DG_LOG", 0))
       std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d gated cfg=%s grid=%d | cfg=%s grid=%d\n", mode,
                    p.rows, p.N, p.K, p.G, dg::config_info(ch.gated_cfg).name, grid_e, ci.name, grid);
-    e = dg::launch_scale_check(p.sfa, na, p.sfb, nb, st->verdicts, stream);
+    e = dg::launch_scale_check(p.sfa, na, p.sfb, nb, r.verdicts, stream);
     if (e == hipSuccess) e = dg::launch_gemm(mode, ch.gated_cfg, pe, grid_e, stream);
   } else if (env_int("DG_LOG", 0)) {
     std::fprintf(stderr, "[dg] mode=%d rows=%d N=%d K=%d G=%d cfg=%s splits=%d kbs=%d grid=%d tail_splits=%d\n",
@@ -384,6 +392,13 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   if (e == hipSuccess && p.sk_splits > 1) e = dg::launch_tile_reduce(mode, ch.cfg, p, grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return DG_OK;
+}
+
+int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
+  DeviceState* st = nullptr;
+  int s = get_device_state(&st);
+  if (s != DG_OK) return s;
+  return launch_with(mode, p, rows_hint, stream, Resources{st->num_cus, st->workspace, kWorkspaceBytes, st->verdicts});
 }
 
 }  // namespace
@@ -629,10 +644,84 @@ extern "C" int dg_choose_config(int form, int rows, int N, int K, int num_groups
   if (rows < 1 || N < 1 || K < 0 || K % 128 != 0 || num_groups < 1 || num_cus < 8 || ab_layout < 0 || ab_layout > 4)
     return fail(DG_ERR_INVALID_ARG, "invalid query (rows=%d N=%d K=%d num_groups=%d num_cus=%d ab_layout=%d)", rows,
                 N, K, num_groups, num_cus, ab_layout);
-  const Choice ch = choose_call(form, rows, N, K, num_groups, num_cus, ab_layout, has_c != 0);
+  const Choice ch = choose_call(form, rows, N, K, num_groups, num_cus, ab_layout, has_c != 0, kWorkspaceBytes);
   *cfg = ch.gated_cfg >= 0 ? ch.gated_cfg : ch.cfg;
   *splits = ch.splits;
   return DG_OK;
+}
+
+// ---- the allocation-free call ------------------------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid it): the kernels' scratch
+// (scale-check verdicts, then split-K partials) lives in a file-scope device
+// array.  In host code `scratch` names a host-side stand-in, not a device
+// address; the device address is taken once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+namespace dg_noalloc {
+constexpr size_t kScratchBytes = size_t(8) << 20;   // per device, held until the process ends
+constexpr size_t kVerdictBytes = 256;                // dg::kCheckWGs int32 verdicts, padded
+static_assert(dg::kCheckWGs * sizeof(int32_t) <= kVerdictBytes, "verdicts fit their area");
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct State {
+  std::atomic<bool> ready{false};
+  int num_cus = 0;
+  uint8_t* ptr = nullptr;       // this device's copy of scratch
+};
+State g_state[kMaxDevices];
+std::mutex g_mu;
+
+int get_state(State** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  State& st = g_state[dev];
+  if (!st.ready.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!st.ready.load(std::memory_order_relaxed)) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+      if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(DG_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950 only", dev, prop.gcnArchName);
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));    // with this device current
+      if (e != hipSuccess || !ptr) return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      st.num_cus = prop.multiProcessorCount;
+      st.ptr = static_cast<uint8_t*>(ptr);
+      st.ready.store(true, std::memory_order_release);
+    }
+  }
+  *out = &st;
+  return DG_OK;
+}
+}  // namespace dg_noalloc
+
+extern "C" int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const float* sfb,
+                                      const void* c, void* d, int M, int N, int K, void* stream) {
+  int s = check_common(a, sfa, b, sfb, c, d, M, N, K);
+  if (s != DG_OK) return s;
+  if (M == 0 || N == 0) return DG_OK;
+  dg_noalloc::State* st = nullptr;
+  s = dg_noalloc::get_state(&st);
+  if (s != DG_OK) return s;
+  dg::Params p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.sfa = sfa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sfb = sfb;
+  p.c = static_cast<const uint16_t*>(c);
+  p.d = static_cast<uint16_t*>(d);
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.G = 1;
+  // the chooser keeps split-K partials within the scratch; a configuration
+  // forced beyond it (DG_FORCE_SPLITS) is refused with DG_ERR_UNSUPPORTED
+  const Resources r{st->num_cus, reinterpret_cast<float*>(st->ptr + dg_noalloc::kVerdictBytes),
+                    dg_noalloc::kScratchBytes - dg_noalloc::kVerdictBytes, reinterpret_cast<int32_t*>(st->ptr)};
+  return launch_with(dg::kDense, p, M, static_cast<hipStream_t>(stream), r);
 }
 
 extern "C" int dg_init(void) {

@@ -51,8 +51,8 @@ def test_version(lib):
 FAKE = ctypes.c_void_p(0x100000)          # aligned, never dereferenced: validation fails first
 
 
-def _dense(lib, a=FAKE, sfa=FAKE, b=FAKE, sfb=FAKE, c=None, d=FAKE, M=64, N=64, K=128):
-    return lib.dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, M, N, K, None)
+def _dense(lib, a=FAKE, sfa=FAKE, b=FAKE, sfb=FAKE, c=None, d=FAKE, M=64, N=64, K=128, fn="dg_fp8_gemm_nt"):
+    return getattr(lib, fn)(a, sfa, b, sfb, c, d, M, N, K, None)
 
 
 @pytest.mark.parametrize("kw,needle", [
@@ -64,14 +64,16 @@ def _dense(lib, a=FAKE, sfa=FAKE, b=FAKE, sfb=FAKE, c=None, d=FAKE, M=64, N=64, 
     (dict(sfb=ctypes.c_void_p(0x100002)), "4-byte"),
     (dict(d=ctypes.c_void_p(0x100001)), "2-byte"),
 ])
-def test_dense_rejects_invalid_arguments(lib, kw, needle):
-    assert _dense(lib, **kw) == _lib.DG_ERR_INVALID_ARG
+@pytest.mark.parametrize("fn", ["dg_fp8_gemm_nt", "dg_fp8_gemm_nt_noalloc"])
+def test_dense_rejects_invalid_arguments(lib, kw, needle, fn):
+    assert _dense(lib, fn=fn, **kw) == _lib.DG_ERR_INVALID_ARG
     assert needle in lib.dg_last_error().decode()
 
 
-def test_dense_empty_is_noop(lib):
-    assert _dense(lib, M=0) == _lib.DG_OK
-    assert _dense(lib, N=0) == _lib.DG_OK
+@pytest.mark.parametrize("fn", ["dg_fp8_gemm_nt", "dg_fp8_gemm_nt_noalloc"])
+def test_dense_empty_is_noop(lib, fn):
+    assert _dense(lib, M=0, fn=fn) == _lib.DG_OK
+    assert _dense(lib, N=0, fn=fn) == _lib.DG_OK
 
 
 def test_grouped_reject_invalid_arguments(lib):
