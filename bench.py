@@ -11,8 +11,18 @@ read from HBM rather than the 256 MB last-level cache; the timed launches are
 replayed from a HIP graph so that host launch cost does not pace the GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes 1,...,13]
+                       [--no-cpu-baseline] [--no-ceilings] [--no-graph]
        python bench.py --calibrate-copy   (a plain device copy of known size, for
                                            scaling HBM byte counters)
+       python bench.py --ceilings         (only the microbenchmarks of libdg_ceilings.so)
+
+Every workload carries a `roofline` block (its bound, the achieved rate per
+call against the MI355X peak: 8 TB/s HBM, 5.0 PFLOP/s dense FP8) and a
+`cpu_baseline`: the CPU oracle timed on the host cores on a bounded sample of
+the same workload (the whole call for small ones; a few rows, groups or one K
+group for the large ones, the rate taken over the sample's own flops).  The
+line also carries a `ceilings` summary measured in the same run (FP8 MFMA loop
+rate, HBM streaming rate, launch cost).
 
 `roofline.traffic` comes from profiles/hbm_traffic.json (HBM bytes per launch
 of the headline kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
@@ -266,26 +276,81 @@ def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool =
     return total, total / steps
 
 
-def cpu_baseline(p, budget_s=10.0):
-    """The oracle as it stands, on the host cores, on the same workload."""
-    import oracle
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def oracle_sample(w):
+    """(callable, algorithmic flops, description) of a bounded sample of
+    workload w for the CPU oracle: whole small calls; for large ones a few
+    rows, a few groups or one K group, whose flops the rate is taken over."""
+    import inputgen
+    import oracle
+    p = w.p
+    small = p.M * p.N * p.K <= (1 << 27) if isinstance(p, (inputgen.Dense, inputgen.DenseFP4)) else False
+    if isinstance(p, inputgen.Dense):
+        rows = np.arange(p.M if small else min(p.M, 64))
+        whole = len(rows) == p.M
+        return (lambda: oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c, rows=rows), 2.0 * len(rows) * p.N * p.K,
+                "the whole call" if whole else f"rows 0-{len(rows) - 1} of {p.M} (all {p.N} columns, all of K)")
+    if isinstance(p, inputgen.DenseFP4):
+        rows = np.arange(p.M if small else min(p.M, 64))
+        whole = len(rows) == p.M
+        return (lambda: oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c, rows=rows), 2.0 * len(rows) * p.N * p.K,
+                "the whole call" if whole else f"rows 0-{len(rows) - 1} of {p.M} (all {p.N} columns, all of K)")
+    if isinstance(p, inputgen.Contiguous):
+        starts = np.concatenate([[0], np.cumsum(((p.counts + 127) // 128) * 128)])
+        groups = [g for g in range(p.G) if p.counts[g] > 0][:2]
+        rows = np.concatenate([np.arange(starts[g], starts[g] + min(64, p.counts[g])) for g in groups])
+        return (lambda: oracle.m_grouped_contiguous(p.a, p.sfa, p.b, p.sfb, p.grouped_layout, rows=rows),
+                2.0 * len(rows) * p.N * p.K, f"{len(rows)} real rows of experts {groups} (all columns, all of K)")
+    if isinstance(p, inputgen.Masked):
+        m = np.minimum(np.maximum(p.masked_m, 0), p.max_m)
+        groups = [g for g in range(p.G) if m[g] > 0][:2]
+        return (lambda: oracle.m_grouped_masked(p.a, p.sfa, p.b, p.sfb, p.masked_m, groups=groups),
+                2.0 * float(m[groups].sum()) * p.N * p.K, f"groups {groups} ({int(m[groups].sum())} rows)")
+    if isinstance(p, inputgen.KGrouped):
+        g = int(np.argmax(p.ks > 0))
+        return (lambda: oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, groups=[g]),
+                2.0 * float(p.counts[g]) * p.M * p.N, f"group {g} ({int(p.ks[g])} K rows)")
+    raise TypeError(p)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on the host cores, timed on a bounded sample
+    of workload w (repeated until budget_s has passed)."""
+    fn, flops, what = oracle_sample(w)
     runs = 0
     t0 = time.perf_counter()
     while True:
-        oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
+        fn()
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 50:
+        if el >= budget_s:
             break
-    per_call = el / runs
-    return {"value": p.flops / per_call / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole headline workload (M={p.M} N={p.N} K={p.K}), {runs} oracle calls "
-                      f"in {el:.1f}s ({per_call * 1e3:.1f} ms per call)"}
+    per = el / runs
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOPS", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{what} of {w.name}: {runs} oracle runs in {el:.1f}s ({per * 1e3:.1f} ms per run, "
+                      f"{flops / 1e9:.2f} GFLOP each)"}
+
+
+def roofline_of(w, ms):
+    """Roofline block of one workload from its measured time per call."""
+    t = load_traffic(w.name)
+    if w.bound == "hbm":
+        achieved = w.bytes / (ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = w.flops / (ms * 1e-3) / 1e12
+        peak, unit = FP8_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": w.bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": int(t["hbm_bytes_per_launch"]) if t else None,
+            "alg_bytes_per_call": int(w.bytes), "alg_flops_per_call": float(w.flops),
+            "avg_call_us": round(ms * 1e3, 3)}
 
 
 def main():
@@ -295,6 +360,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--shapes", default="1,2,3,4,5,6,7,8,9,10,11,12,13", help="comma-separated 1-based workload indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="leave the microbenchmark summary out of the line")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--calibrate-copy", action="store_true", help="run only the copy used to scale byte counters")
     ap.add_argument("--ceilings", action="store_true",
@@ -327,6 +393,7 @@ def main():
 
     per_shape = {}
     head = None
+    baselines = {}          # cpu_baseline by generated problem (entries that reuse one share it)
     for idx in shapes:
         w = Workload(idx, torch, dg)
         steps = args.steps
@@ -340,10 +407,16 @@ def main():
                "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
                "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                "bound": w.bound, "alg_bytes": int(w.bytes), "flops": float(w.flops),
-               "steps": steps, "copies": w.copies}
+               "steps": steps, "copies": w.copies, "roofline": roofline_of(w, ms)}
         per_shape[w.name] = rec
         log(f"[bench] {w.name}: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / FP8_PEAK_TFLOPS:.1f}% "
             f"of FP8 peak), {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+        if not args.no_cpu_baseline:
+            src = PROBLEM_OF.get(idx, idx)
+            if src not in baselines:
+                baselines[src] = cpu_baseline(w, 10.0 if idx == HEADLINE else 2.0)
+                log(f"[bench] {w.name}: oracle on the host, {baselines[src]['sample']}")
+            rec["cpu_baseline"] = baselines[src]
         if idx == HEADLINE:
             head = (w, steps, total_ms, ms, tflops, gbs)
             if reps:
@@ -354,16 +427,23 @@ def main():
             torch.cuda.empty_cache()
 
     w, steps, total_ms, ms, tflops, gbs = head
-    t = load_traffic(w.name)
-    traffic = int(t["hbm_bytes_per_launch"]) if t else None
-    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": int(w.bytes), "avg_launch_us": round(ms * 1e3, 3),
-                "kernel": "fp8_gemm_nt_decode_kernel + splitk_reduce_kernel (two launches per call, timed together)"}
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on the headline workload")
-        cpu = cpu_baseline(w.p)
+    roofline = dict(roofline_of(w, ms))
+    roofline["kernel"] = ("fp8_gemm_nt_decode_kernel + splitk_reduce_kernel: the two launches of one call, "
+                          "timed together (per-call time)")
+    cpu = per_shape[w.name].get("cpu_baseline")
+    ceil = None
+    if not args.no_ceilings:
+        try:
+            from moe_grouped_gemm_nt_amd import ceilings
+            c = ceilings.measure(torch)
+            ceil = {"mfma_fp8_chained_pflops": max(v for k, v in c.items() if k.startswith("mfma_fp8_chained")),
+                    "mfma_fp8_promoted_pflops": max(v for k, v in c.items() if k.startswith("mfma_fp8_promoted")),
+                    "hbm_stream_gbs": max(c["hbm_bulk_4wg_per_cu_1MiB"]["gbs"], c["hbm_bulk_4wg_per_cu_1MiB_vgpr16"]["gbs"]),
+                    "empty_kernel_us": c["empty_kernel_us_per_launch"],
+                    "stream_15MiB_one_launch_us": c["hbm_1wg_per_cu_60KiB_lds31"]["us_per_launch"],
+                    "source": "bench.py --ceilings (libdg_ceilings.so)"}
+        except Exception as e:  # the summary is context; its absence does not void the measurement
+            log(f"[bench] ceilings not measured: {e}")
     line = {
         "metric": "FP8 block-scaled GEMM TFLOPS + % of MI355X dense FP8 peak, per shape",
         "value": round(tflops, 2),
@@ -386,6 +466,7 @@ def main():
                    "graph_replay": not args.no_graph, "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "per_shape": per_shape,
     }
     print(json.dumps(line), flush=True)
