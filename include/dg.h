@@ -210,6 +210,20 @@ int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const
 int dg_choose_config(int form, int rows, int N, int K, int num_groups, int num_cus, int ab_layout,
                      int has_c, int* cfg, int* splits);
 
+/* Host-side check of a contiguous grouped_layout held in HOST memory (M int32
+ * entries) against the contract of the contiguous calls: within every aligned
+ * block of 128 rows, all rows whose id lies in [0, num_groups) carry the same
+ * id.  Returns DG_OK, or DG_ERR_INVALID_ARG with dg_last_error() naming the
+ * first offending block.  Touches no device.
+ *
+ * Debug mode: with the environment variable DG_VALIDATE=1, the M-grouped calls
+ * copy their device-resident grouped_layout (or masked_m) to the host on the
+ * call's stream, wait for it, and apply this check (masked: every masked_m[g]
+ * within [0, max_m], which the kernels would otherwise clamp) before launching
+ * anything; a violation returns DG_ERR_INVALID_ARG.  It synchronises, so it is
+ * for debugging only, and it is skipped while the stream is being captured. */
+int dg_check_grouped_layout(const int32_t* grouped_layout, int M, int num_groups);
+
 /* Prepares per-device state for the current HIP device (device properties and
  * the split-K workspace, allocated once and kept until the process ends).
  * Calls above do this lazily on first use; call dg_init() first when the

@@ -32,6 +32,7 @@ EXPORTED = [
     "dg_m_grouped_fp8_fp4_gemm_nt_masked",
     "dg_k_grouped_fp8_gemm_tn_contiguous",
     "dg_choose_config",
+    "dg_check_grouped_layout",
     "dg_init",
     "dg_last_error",
     "dg_version",
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = ci
         lib.dg_choose_config.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
         lib.dg_choose_config.restype = ci
+        lib.dg_check_grouped_layout.argtypes = [vp, ci, ci]
+        lib.dg_check_grouped_layout.restype = ci
         lib.dg_init.argtypes = []
         lib.dg_init.restype = ci
         lib.dg_last_error.argtypes = []
@@ -165,6 +168,17 @@ def dg_choose_config(form, rows, N, K, num_groups=1, num_cus=256, ab_layout="nt"
         FORMS[form], int(rows), int(N), int(K), int(num_groups), int(num_cus), AB_LAYOUTS[ab_layout],
         1 if has_c else 0, ctypes.byref(cfg), ctypes.byref(splits)))
     return cfg.value, splits.value
+
+
+def dg_check_grouped_layout(grouped_layout, num_groups) -> None:
+    """Host-side check of a contiguous layout (a host int32 array or tensor) against
+    the one-expert-per-128-row-block contract; raises DGError naming the first
+    offending block."""
+    import numpy as np
+    h = np.ascontiguousarray(np.asarray(grouped_layout.cpu() if isinstance(grouped_layout, torch.Tensor)
+                                        else grouped_layout, dtype=np.int32))
+    _check("dg_check_grouped_layout", load().dg_check_grouped_layout(
+        h.ctypes.data_as(ctypes.c_void_p), int(h.size), int(num_groups)))
 
 
 def dg_version() -> int:

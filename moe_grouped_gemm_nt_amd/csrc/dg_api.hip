@@ -36,6 +36,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/dg.h"
 #include "dg_internal.h"
@@ -111,6 +112,63 @@ int check_common(const void* a, const float* sfa, const void* b, const float* sf
   if (!aligned(a, 16) || !aligned(b, 16)) return fail(DG_ERR_INVALID_ARG, "a and b must be 16-byte aligned");
   if (!aligned(sfa, 4) || !aligned(sfb, 4)) return fail(DG_ERR_INVALID_ARG, "sfa and sfb must be 4-byte aligned");
   if (!aligned(d, 2) || (c && !aligned(c, 2))) return fail(DG_ERR_INVALID_ARG, "c and d must be 2-byte aligned");
+  return DG_OK;
+}
+
+// The contiguous layout's contract on host data: in every aligned block of
+// 128 rows, all rows whose id lies in [0, G) carry the same id.
+int check_layout_host(const int32_t* layout, int M, int G) {
+  for (int b = 0; b * 128 < M; ++b) {
+    int id = -1;
+    for (int r = b * 128; r < M && r < (b + 1) * 128; ++r) {
+      const int v = layout[r];
+      if (v < 0 || v >= G) continue;
+      if (id >= 0 && v != id)
+        return fail(DG_ERR_INVALID_ARG,
+                    "grouped_layout: rows %d..%d (one 128-row block) hold experts %d and %d; a block may hold one",
+                    b * 128, std::min(M, (b + 1) * 128) - 1, id, v);
+      id = v;
+    }
+  }
+  return DG_OK;
+}
+
+// DG_VALIDATE=1: copies device control data to the host (on the call's
+// stream, then waits for it) and checks it before anything is launched.  A
+// debugging aid: it synchronises, so it is skipped while the stream is being
+// captured into a graph.
+bool validate_on(hipStream_t stream) {
+  const char* v = std::getenv("DG_VALIDATE");
+  if (!v || !*v || *v == '0') return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return false;
+  return cs == hipStreamCaptureStatusNone;
+}
+
+int copy_to_host(std::vector<int32_t>& dst, const int32_t* src, int n, hipStream_t stream) {
+  dst.assign((size_t)n, 0);
+  hipError_t e = hipMemcpyAsync(dst.data(), src, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "DG_VALIDATE: reading device data: %s", hipGetErrorString(e));
+  return DG_OK;
+}
+
+int validate_layout(const int32_t* layout, int M, int G, hipStream_t stream) {
+  if (!validate_on(stream)) return DG_OK;
+  std::vector<int32_t> h;
+  int s = copy_to_host(h, layout, M, stream);
+  return s != DG_OK ? s : check_layout_host(h.data(), M, G);
+}
+
+int validate_masked(const int32_t* masked_m, int G, int max_m, hipStream_t stream) {
+  if (!validate_on(stream)) return DG_OK;
+  std::vector<int32_t> h;
+  int s = copy_to_host(h, masked_m, G, stream);
+  if (s != DG_OK) return s;
+  for (int g = 0; g < G; ++g)
+    if (h[g] < 0 || h[g] > max_m)
+      return fail(DG_ERR_INVALID_ARG, "masked_m[%d] = %d lies outside [0, max_m = %d] (the kernels would clamp it)", g,
+                  h[g], max_m);
   return DG_OK;
 }
 
@@ -563,6 +621,8 @@ int grouped_contiguous(const void* a, const float* sfa, const void* b, const flo
   if (!grouped_layout) return fail(DG_ERR_INVALID_ARG, "grouped_layout must not be NULL");
   if (!aligned(grouped_layout, 4)) return fail(DG_ERR_INVALID_ARG, "grouped_layout must be 4-byte aligned");
   if (M == 0 || N == 0) return DG_OK;
+  s = validate_layout(grouped_layout, M, num_groups, static_cast<hipStream_t>(stream));
+  if (s != DG_OK) return s;
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
   p.sfa = sfa;
@@ -590,6 +650,8 @@ int grouped_masked(const void* a, const float* sfa, const void* b, const float* 
   if (!aligned(masked_m, 4)) return fail(DG_ERR_INVALID_ARG, "masked_m must be 4-byte aligned");
   if (expected_m < 0) return fail(DG_ERR_INVALID_ARG, "expected_m=%d must not be negative", expected_m);
   if (max_m == 0 || N == 0) return DG_OK;
+  s = validate_masked(masked_m, num_groups, max_m, static_cast<hipStream_t>(stream));
+  if (s != DG_OK) return s;
   dg::Params p{};
   p.a = static_cast<const uint8_t*>(a);
   p.sfa = sfa;
@@ -722,6 +784,12 @@ extern "C" int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const voi
   const Resources r{st->num_cus, reinterpret_cast<float*>(st->ptr + dg_noalloc::kVerdictBytes),
                     dg_noalloc::kScratchBytes - dg_noalloc::kVerdictBytes, reinterpret_cast<int32_t*>(st->ptr)};
   return launch_with(dg::kDense, p, M, static_cast<hipStream_t>(stream), r);
+}
+
+extern "C" int dg_check_grouped_layout(const int32_t* grouped_layout, int M, int num_groups) {
+  if (!grouped_layout && M > 0) return fail(DG_ERR_INVALID_ARG, "grouped_layout must not be NULL");
+  if (M < 0 || num_groups < 1) return fail(DG_ERR_INVALID_ARG, "M=%d num_groups=%d", M, num_groups);
+  return check_layout_host(grouped_layout, M, num_groups);
 }
 
 extern "C" int dg_init(void) {

@@ -200,6 +200,50 @@ __device__ __forceinline__ void mma_block(const uint8_t* a_rows, int arow0, cons
   }
 }
 
+// Masked form: s_prefix[g] = work items of the groups before g (their m-tiles
+// of BM rows times the n-tiles), s_prefix[G] = all items, with masked_m
+// clamped to [0, max_m].  Every thread of the NT-thread workgroup loads the
+// masked_m of its own run of consecutive groups (all loads in flight at once,
+// one memory round trip), then a workgroup-wide exclusive scan: an inclusive
+// scan inside each wave by lane shuffles, the wave totals through LDS.
+// Ends with a workgroup barrier; s_prefix then holds the list.
+template <int BM, int NT>
+__device__ __forceinline__ void masked_prefix(const Params& p, int* s_prefix, int tid) {
+  constexpr int GPT = (MAX_GROUPS_LDS + NT) / NT;        // groups per thread (entries 0..G, G <= MAX_GROUPS_LDS)
+  constexpr int NW = NT / 64;
+  static_assert(NT % 64 == 0 && NW <= 64, "whole waves");
+  __shared__ int s_wave[NW];
+  int cnt[GPT];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int g = tid * GPT + i;
+    int m = g < p.G ? p.masked_m[g] : 0;
+    m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
+    cnt[i] = ((m + BM - 1) / BM) * p.tiles_n;
+    local += cnt[i];
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  int run = before + incl - local;          // exclusive prefix of this thread's first group
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int g = tid * GPT + i;
+    if (g <= p.G) s_prefix[g] = run;        // g == G receives the total
+    run += cnt[i];
+  }
+  __syncthreads();
+}
+
 // Output tile of linear tile id `tile` in the grouped order: bands of 8
 // m-tiles sweep across n, so consecutive tiles share B columns.
 __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& mt, int& nt) {
@@ -425,17 +469,7 @@ fp8_gemm_nt_kernel(PT p) {
   int total;
   if constexpr (MODE == kMasked) {
     // exclusive prefix over groups of (m tiles * n tiles); masked_m clamped to [0, max_m]
-    if (tid == 0) {
-      int acc = 0;
-      for (int g = 0; g < p.G; ++g) {
-        int m = p.masked_m[g];
-        m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
-        s_prefix[g] = acc;
-        acc += ((m + BM - 1) / BM) * p.tiles_n;
-      }
-      s_prefix[p.G] = acc;
-    }
-    __syncthreads();
+    masked_prefix<BM, S::NT>(p, s_prefix, tid);
     total = s_prefix[p.G];
   } else if constexpr (KG) {
     total = p.G * p.tiles_m * p.tiles_n;

@@ -62,17 +62,7 @@ fp8_gemm_nt_ws_kernel(Params p) {
 
   int total;
   if constexpr (MODE == kMasked) {
-    if (tid == 0) {
-      int acc = 0;
-      for (int g = 0; g < p.G; ++g) {
-        int m = p.masked_m[g];
-        m = m < 0 ? 0 : (m > p.rows ? p.rows : m);
-        s_prefix[g] = acc;
-        acc += ((m + BM - 1) / BM) * p.tiles_n;
-      }
-      s_prefix[p.G] = acc;
-    }
-    __syncthreads();
+    masked_prefix<BM, 2 * S::NT>(p, s_prefix, tid);     // MFMA and loader waves together
     total = s_prefix[p.G];
   } else {
     total = p.tiles_m * p.tiles_n;

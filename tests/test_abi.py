@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import moe_grouped_gemm_nt_amd as dgpkg
@@ -163,3 +164,16 @@ def test_ceilings_library_exports_every_declared_symbol():
     assert lib.dgc_mfma(0, 1, 0, ctypes.c_void_p(0x1000), None) == -1
     assert lib.dgc_chase(ctypes.c_void_p(0x1000), 10, 3, ctypes.c_void_p(0x1000), None) == -1
     assert lib.dgc_chase(None, 10, 0, ctypes.c_void_p(0x1000), None) == -1
+
+
+def test_layout_check_on_host(lib):
+    ok = np.array([0] * 128 + [1] * 100 + [-1] * 28 + [7] * 20, dtype=np.int32)
+    dgpkg.dg_check_grouped_layout(ok, 2)                  # ids >= G count as padding
+    bad = np.array([0] * 100 + [1] * 28 + [1] * 10, dtype=np.int32)
+    with pytest.raises(dgpkg.DGError) as e:
+        dgpkg.dg_check_grouped_layout(bad, 2)
+    assert e.value.status == _lib.DG_ERR_INVALID_ARG and "rows 0..127" in str(e.value)
+    tail = np.array([3] * 128 + [3] * 5 + [0] * 2, dtype=np.int32)   # the ragged last block
+    with pytest.raises(dgpkg.DGError) as e:
+        dgpkg.dg_check_grouped_layout(tail, 4)
+    assert "rows 128..134" in str(e.value)
