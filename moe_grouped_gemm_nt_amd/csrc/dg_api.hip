@@ -282,7 +282,14 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
       else if (c128x256 <= c128) ch.cfg = dg::kCfg128x256w8;
       else ch.cfg = dg::kCfg128x128;
     } else if (mode != dg::kContiguous && !(masked && rows < 128) && tiles256 >= num_cus) {
-      ch.cfg = dg::kCfg256x256w8;
+      // masked groups of 128 to 191 expected rows: 256x128 tiles (three
+      // K blocks in the ring instead of two, and rows idle in 64-row wave
+      // rows past a group's end) measured 4% faster than 256x256 at 32
+      // groups of 0-256 rows (N 4096, K 7168), the same at 128-256 rows, and
+      // slower for larger groups (FP8 B only: no FP4 build of that tile)
+      const long long tiles256x128 = g * (((long long)rows + 255) / 256) * ((N + 127) / 128);
+      ch.cfg = masked && rows < 192 && ab_layout == 0 && tiles256x128 >= num_cus ? dg::kCfg256x128w8
+                                                                                    : dg::kCfg256x256w8;
     } else if (tiles128x256 >= num_cus) {
       ch.cfg = dg::kCfg128x256w8;
     } else {

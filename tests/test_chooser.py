@@ -3,8 +3,8 @@ code only, no device): the benchmark's workloads get the kernels their
 measurements favour, and the forced-configuration switch acts as on the calls.
 
 Configuration ids: 0 128x128, 1 decode (64x64 tiles, K split over
-workgroups), 6 128x256, 7 128x256 with power-of-two scales in the MFMA,
-9 narrow (16x48 over the whole K), 11 256x256."""
+workgroups), 5 256x128, 6 128x256, 7 128x256 with power-of-two scales in the
+MFMA, 9 narrow (16x48 over the whole K), 11 256x256."""
 import pytest
 
 import moe_grouped_gemm_nt_amd as dg
@@ -30,8 +30,11 @@ def no_forcing(monkeypatch):
     ("dense", 4096, 7168, 16384, 1, "fp4", False, (11, 1)),
     # contiguous calls keep 128-row tiles
     ("contiguous", 8704, 4096, 7168, 8, "nt", False, (6, 1)),
-    # masked: 32 groups of about 128 rows, 512 256x256 tiles
-    ("masked", 128, 4096, 7168, 32, "nt", False, (11, 1)),
+    # masked: 32 groups of about 128 rows: 256x128 tiles (three K blocks in
+    # flight); larger groups 256x256; an FP4 B keeps 256x256
+    ("masked", 128, 4096, 7168, 32, "nt", False, (5, 1)),
+    ("masked", 192, 4096, 7168, 32, "nt", False, (11, 1)),
+    ("masked", 128, 4096, 7168, 32, "fp4", False, (11, 1)),
     # masked, 8 groups of 16 rows: 128 tiles of 128x256 leave half the CUs idle
     ("masked", 16, 4096, 7168, 8, "nt", False, (0, 1)),
     # at most 16 rows and 16x48 tiles for half the CUs: the narrow kernel
