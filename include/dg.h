@@ -38,10 +38,11 @@
  * synchronisation, as for any HIP kernel.
  *
  * All calls on one device share its split-K workspace (fp32 partial tiles)
- * and its scale-check results.  Calls enqueued on one stream, or ordered
- * across streams by events, are safe; calls that may run at the same time on
- * different streams of one device race on that memory and must be ordered by
- * the caller.
+ * and its scale-check results, unless their stream has a workspace of its own
+ * (dg_bind_stream_workspace).  Calls enqueued on one stream, or ordered across
+ * streams by events, are safe; calls that may run at the same time on
+ * different streams of one device race on the shared memory and must be
+ * ordered by the caller, or given per-stream workspaces.
  *
  * Errors: an invalid argument returns DG_ERR_INVALID_ARG and launches nothing;
  * a shape the kernels do not handle returns DG_ERR_UNSUPPORTED; a failing HIP
@@ -51,6 +52,7 @@
 #ifndef DG_H
 #define DG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -209,6 +211,21 @@ int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const
  * outside 0-4; DG_OK otherwise. */
 int dg_choose_config(int form, int rows, int N, int K, int num_groups, int num_cus, int ab_layout,
                      int has_c, int* cfg, int* splits);
+
+/* Binds a caller-owned device workspace to a stream of the current device:
+ * every later call of this library enqueued on that stream uses it in place
+ * of the device's shared workspace (split-K partial tiles and scale-check
+ * verdicts), so that calls running at the same time on different streams no
+ * longer share scratch memory.  workspace: device memory on the current
+ * device, 256-byte aligned, at least 256 bytes (the verdicts); the rest holds
+ * partials, and the configuration is chosen so that they fit (a bound
+ * workspace of a few hundred bytes simply means no split-K).  The caller keeps
+ * the memory alive, and unused by anything else, while the binding lasts and
+ * while calls enqueued with it run.  workspace NULL (or bytes 0) removes the
+ * stream's binding.  The allocation-free call (dg_fp8_gemm_nt_noalloc) always
+ * uses its own fixed array.  Returns DG_ERR_INVALID_ARG for a misaligned or
+ * too small workspace, DG_ERR_HIP if the current device cannot be queried. */
+int dg_bind_stream_workspace(void* stream, void* workspace, size_t bytes);
 
 /* Host-side check of a contiguous grouped_layout held in HOST memory (M int32
  * entries) against the contract of the contiguous calls: within every aligned

@@ -6,6 +6,7 @@ from ._lib import (  # noqa: F401
     DGError,
     EXPORTED,
     LIB_PATH,
+    dg_bind_stream_workspace,
     dg_check_grouped_layout,
     dg_choose_config,
     dg_fp8_fp4_gemm_nt,

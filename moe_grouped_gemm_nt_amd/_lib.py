@@ -33,6 +33,7 @@ EXPORTED = [
     "dg_k_grouped_fp8_gemm_tn_contiguous",
     "dg_choose_config",
     "dg_check_grouped_layout",
+    "dg_bind_stream_workspace",
     "dg_init",
     "dg_last_error",
     "dg_version",
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dg_k_grouped_fp8_gemm_tn_contiguous.restype = ci
         lib.dg_choose_config.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
         lib.dg_choose_config.restype = ci
+        lib.dg_bind_stream_workspace.argtypes = [vp, vp, ctypes.c_size_t]
+        lib.dg_bind_stream_workspace.restype = ci
         lib.dg_check_grouped_layout.argtypes = [vp, ci, ci]
         lib.dg_check_grouped_layout.restype = ci
         lib.dg_init.argtypes = []
@@ -168,6 +171,19 @@ def dg_choose_config(form, rows, N, K, num_groups=1, num_cus=256, ab_layout="nt"
         FORMS[form], int(rows), int(N), int(K), int(num_groups), int(num_cus), AB_LAYOUTS[ab_layout],
         1 if has_c else 0, ctypes.byref(cfg), ctypes.byref(splits)))
     return cfg.value, splits.value
+
+
+def dg_bind_stream_workspace(stream, workspace) -> None:
+    """Binds a device tensor (256-byte aligned, at least 256 bytes) as the
+    workspace of every later call on `stream`; workspace None removes the binding."""
+    if workspace is None:
+        ptr, nbytes = None, 0
+    else:
+        _on_device(workspace=workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check("dg_bind_stream_workspace", load().dg_bind_stream_workspace(_stream(stream), ptr, nbytes))
 
 
 def dg_check_grouped_layout(grouped_layout, num_groups) -> None:

@@ -459,11 +459,43 @@ int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, cons
   return DG_OK;
 }
 
+// Caller-supplied workspaces bound to streams (dg_bind_stream_workspace):
+// calls enqueued on a bound stream of that device use it in place of the
+// device's shared workspace.
+constexpr size_t kBoundVerdictBytes = 256;      // the first bytes of a bound workspace hold the verdicts
+struct Binding {
+  int dev;
+  hipStream_t stream;
+  uint8_t* ptr;
+  size_t bytes;
+};
+std::vector<Binding> g_bindings;
+std::mutex g_bind_mu;
+std::atomic<int> g_nbind{0};        // bindings in g_bindings (read without the lock)
+
+bool find_binding(int dev, hipStream_t stream, Binding* out) {
+  std::lock_guard<std::mutex> lock(g_bind_mu);
+  for (const Binding& b : g_bindings)
+    if (b.dev == dev && b.stream == stream) {
+      *out = b;
+      return true;
+    }
+  return false;
+}
+
 int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   DeviceState* st = nullptr;
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
-  return launch_with(mode, p, rows_hint, stream, Resources{st->num_cus, st->workspace, kWorkspaceBytes, st->verdicts});
+  Resources r{st->num_cus, st->workspace, kWorkspaceBytes, st->verdicts};
+  int dev = 0;
+  Binding b;
+  if (g_nbind.load(std::memory_order_acquire) > 0 && hipGetDevice(&dev) == hipSuccess && find_binding(dev, stream, &b)) {
+    r.verdicts = reinterpret_cast<int32_t*>(b.ptr);
+    r.workspace = reinterpret_cast<float*>(b.ptr + kBoundVerdictBytes);
+    r.ws_bytes = b.bytes - kBoundVerdictBytes;
+  }
+  return launch_with(mode, p, rows_hint, stream, r);
 }
 
 }  // namespace
@@ -791,6 +823,27 @@ extern "C" int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const voi
   const Resources r{st->num_cus, reinterpret_cast<float*>(st->ptr + dg_noalloc::kVerdictBytes),
                     dg_noalloc::kScratchBytes - dg_noalloc::kVerdictBytes, reinterpret_cast<int32_t*>(st->ptr)};
   return launch_with(dg::kDense, p, M, static_cast<hipStream_t>(stream), r);
+}
+
+extern "C" int dg_bind_stream_workspace(void* stream, void* workspace, size_t bytes) {
+  if (workspace && !aligned(workspace, 256))
+    return fail(DG_ERR_INVALID_ARG, "the workspace must be 256-byte aligned");
+  if (workspace && bytes < kBoundVerdictBytes)
+    return fail(DG_ERR_INVALID_ARG, "a workspace of %zu bytes is smaller than the %zu the verdicts need", bytes,
+                kBoundVerdictBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_bind_mu);
+  for (size_t i = 0; i < g_bindings.size(); ++i)
+    if (g_bindings[i].dev == dev && g_bindings[i].stream == st) {
+      g_bindings.erase(g_bindings.begin() + (long)i);
+      break;
+    }
+  if (workspace && bytes > 0) g_bindings.push_back(Binding{dev, st, static_cast<uint8_t*>(workspace), bytes});
+  g_nbind.store((int)g_bindings.size(), std::memory_order_release);
+  return DG_OK;
 }
 
 extern "C" int dg_check_grouped_layout(const int32_t* grouped_layout, int M, int num_groups) {

@@ -177,3 +177,11 @@ def test_layout_check_on_host(lib):
     with pytest.raises(dgpkg.DGError) as e:
         dgpkg.dg_check_grouped_layout(tail, 4)
     assert "rows 128..134" in str(e.value)
+
+
+def test_stream_workspace_binding_rejects_bad_buffers(lib):
+    lib.dg_bind_stream_workspace.restype = ctypes.c_int
+    assert lib.dg_bind_stream_workspace(None, ctypes.c_void_p(0x100010), ctypes.c_size_t(1 << 20)) == _lib.DG_ERR_INVALID_ARG
+    assert "256-byte" in lib.dg_last_error().decode()
+    assert lib.dg_bind_stream_workspace(None, ctypes.c_void_p(0x100000), ctypes.c_size_t(128)) == _lib.DG_ERR_INVALID_ARG
+    assert "smaller" in lib.dg_last_error().decode()

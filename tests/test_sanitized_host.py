@@ -120,6 +120,11 @@ DRIVER = textwrap.dedent(r"""
     assert b"rows 0..127" in lib.dg_last_error()
     expect(chk(None, 10, 2), -1, "null layout")
     expect(chk(None, 0, 2), 0, "empty layout")
+    bind = lib.dg_bind_stream_workspace
+    bind.restype = ci
+    bind.argtypes = [vp, vp, ctypes.c_size_t]
+    expect(bind(None, vp(0x100010), 1 << 20), -1, "misaligned workspace")
+    expect(bind(None, F, 100), -1, "workspace too small")
     print(f"SANITIZED_OK {calls}")
 """)
 
