@@ -277,10 +277,10 @@ def time_workload(torch, w: Workload, steps: int, warmup: int, use_graph: bool =
 
 
 def warm_gpu(torch, seconds=0.3):
-    """Keeps the matrix cores busy for a fraction of a second before anything
-    is timed: the clock ramps up under load, and without this the first
-    workload timed measured up to 8% slower than the same configuration timed
-    later in the run."""
+    """Keeps the matrix cores busy for a fraction of a second before a workload
+    is timed: the clock ramps up under load, and a workload timed right after
+    the seconds of host work that generate its inputs (the GPU idle) measured
+    up to 8% slower than the same configuration timed again at once."""
     try:
         from moe_grouped_gemm_nt_amd import ceilings
         lib = ceilings.load()
@@ -418,6 +418,9 @@ def main():
     baselines = {}          # cpu_baseline by generated problem (entries that reuse one share it)
     for idx in shapes:
         w = Workload(idx, torch, dg)
+        # generating and uploading a workload leaves the GPU idle for seconds;
+        # bring the clock back up before its warm-up steps and timing
+        warm_gpu(torch, 0.2)
         steps = args.steps
         if w.flops > 1e11:
             steps = max(10, min(steps, 50))         # large shapes: keep the timed region short
