@@ -466,6 +466,7 @@ def main():
                     "hbm_stream_gbs": max(c["hbm_bulk_4wg_per_cu_1MiB"]["gbs"], c["hbm_bulk_4wg_per_cu_1MiB_vgpr16"]["gbs"]),
                     "empty_kernel_us": c["empty_kernel_us_per_launch"],
                     "stream_15MiB_one_launch_us": c["hbm_1wg_per_cu_60KiB_lds31"]["us_per_launch"],
+                    "lds_fill_l2_shared_tbs": c["fill_8waves_shared_by_8_per_xcd"]["tbs"],
                     "source": "bench.py --ceilings (libdg_ceilings.so)"}
         except Exception as e:  # the summary is context; its absence does not void the measurement
             log(f"[bench] ceilings not measured: {e}")

@@ -24,6 +24,13 @@ extern "C" {
  * sink: int32 [grid], written by mode 0 and 1 only. */
 int dgc_stream(const void* src, long bytes_per_wg, int grid, int mode, int* sink, void* stream);
 
+/* 256 workgroups of eight waves in groups of `share` workgroups of one XCD
+ * (share divides 32; workgroup i is on XCD i % 8): group g reads the steps
+ * 64 KB blocks at src + g * group_bytes (steps * 65536 <= group_bytes) with
+ * direct global->LDS loads, 8 in flight per wave.  The caller's buffer must
+ * hold (256 / share) * group_bytes bytes.  sink: int32 [256]. */
+int dgc_fill(const void* src, long group_bytes, int steps, int share, int* sink, void* stream);
+
 /* grid workgroups of 256 threads that do nothing. */
 int dgc_empty(int grid, void* stream);
 

@@ -26,7 +26,8 @@ def load():
         lib.dgc_empty.argtypes = [ci, vp]
         lib.dgc_mfma.argtypes = [ci, ci, ci, vp, vp]
         lib.dgc_chase.argtypes = [vp, ci, ci, vp, vp]
-        for f in (lib.dgc_stream, lib.dgc_empty, lib.dgc_mfma, lib.dgc_chase):
+        lib.dgc_fill.argtypes = [vp, cl, ci, ci, vp, vp]
+        for f in (lib.dgc_stream, lib.dgc_empty, lib.dgc_mfma, lib.dgc_chase, lib.dgc_fill):
             f.restype = ci
         _lib = lib
     return _lib
@@ -143,6 +144,23 @@ def measure(torch, num_cus=None):
                      "gbs_per_cu": round(per / (us * 1e-6) / 1e9 / num_cus, 2),
                      "gbs_beyond_empty_launch": round(per / (max(us - empty_us, 1e-3) * 1e-6) / 1e9, 1),
                      "mode": modes[mode]}
+    # the tile kernels' load shape without their K-block barriers: 256
+    # workgroups of eight waves streaming 64 KB blocks, 8 loads in flight per
+    # wave; `share` workgroups of one XCD read the same blocks (from the L2
+    # after the first), as the tiles of one XCD share A and B rows
+    fsink = torch.empty(256, dtype=torch.int32, device="cuda")
+    for name, share, steps in (("fill_8waves_distinct_hbm", 1, 64), ("fill_8waves_shared_by_8_per_xcd", 8, 128),
+                               ("fill_8waves_shared_by_32_per_xcd", 32, 128)):
+        group_bytes = steps * 65536
+        assert (256 // share) * group_bytes <= buf.numel()
+        n = 4
+        ms = _time_graph(torch, [lambda s, sh=share, st=steps, gb=group_bytes: _ok(lib.dgc_fill(
+            ctypes.c_void_p(buf.data_ptr()), gb, st, sh, ctypes.c_void_p(fsink.data_ptr()), s), "dgc_fill")] * n)
+        us = ms * 1e3 / n
+        filled = 256 * steps * 65536
+        out[name] = {"us_per_launch": round(us, 3), "bytes_into_lds": filled,
+                     "tbs": round(filled / (us * 1e-6) / 1e12, 2),
+                     "gbs_per_cu": round(filled / (us * 1e-6) / 1e9 / num_cus, 1)}
     del buf
     torch.cuda.empty_cache()
     word = torch.zeros(64, dtype=torch.int32, device="cuda")

@@ -76,6 +76,34 @@ __global__ void __launch_bounds__(256) stream_kernel(const uint8_t* __restrict__
   }
 }
 
+// 256 workgroups of eight waves, the tile kernels' shape.  The workgroups of
+// one XCD (blockIdx % 8) form groups of `share` (32 / share groups per XCD);
+// group g reads the `steps` 64 KB blocks at src + g * group_bytes, each block
+// 64 direct global->LDS loads of 1 KB spread over the waves (8 each), 8
+// loads in flight per wave and no barrier: with share > 1 most of the bytes
+// come from the L2, which the group's workgroups share as a tile kernel's
+// workgroups share A and B rows.
+__global__ void __launch_bounds__(512) fill_kernel(const uint8_t* __restrict__ src, long group_bytes, int steps,
+                                                   int share, int* __restrict__ sink) {
+  constexpr int INFL = 8, RING = INFL + 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[8 * RING * 1024];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = (blockIdx.x % 8) * (32 / share) + (blockIdx.x / 8) / share;
+  const uint8_t* base = src + (long)group * group_bytes + lane * 16;
+  const uint32_t r0 = lds_addr(ring) + (uint32_t)(wave * RING * 1024);
+  const int n = steps * 8;
+  auto addr = [&](int i) { return base + (long)((i / 8) * 64 + wave * 8 + i % 8) * 1024; };
+  int i = 0;
+  for (; i < n && i < INFL; ++i) dma_16(addr(i), r0 + (uint32_t)(i % RING) * 1024);
+  for (; i < n; ++i) {
+    wait_vm<INFL - 1>();
+    dma_16(addr(i), r0 + (uint32_t)(i % RING) * 1024);
+  }
+  wait_vm<0>();
+  if (threadIdx.x == 0) sink[blockIdx.x] = n;
+}
+
 __global__ void __launch_bounds__(256) empty_kernel() {}
 
 // Back-to-back 16x16x128 FP8 MFMAs on register operands, eight independent
@@ -155,6 +183,15 @@ extern "C" int dgc_stream(const void* src, long bytes_per_wg, int grid, int mode
     case 2: hipLaunchKernelGGL((stream_kernel<false, 8>), dim3(grid), dim3(256), 0, s, p, bytes_per_wg, sink); break;
     case 3: hipLaunchKernelGGL((stream_kernel<false, 16>), dim3(grid), dim3(256), 0, s, p, bytes_per_wg, sink); break;
   }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int dgc_fill(const void* src, long group_bytes, int steps, int share, int* sink, void* stream) {
+  if (!src || !sink || steps < 1 || share < 1 || share > 32 || 32 % share != 0 ||
+      (long)steps * 65536 > group_bytes)
+    return -1;
+  hipLaunchKernelGGL(fill_kernel, dim3(256), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(src), group_bytes, steps, share, sink);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -153,7 +153,7 @@ def test_ceilings_library_exports_every_declared_symbol():
         build.build_ceilings()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dg_ceilings.h")).read(), flags=re.S)
     syms = sorted(set(re.findall(r"\b(dgc_[a-z0-9_]+)\s*\(", text)))
-    assert syms == ["dgc_chase", "dgc_empty", "dgc_mfma", "dgc_stream"]
+    assert syms == ["dgc_chase", "dgc_empty", "dgc_fill", "dgc_mfma", "dgc_stream"]
     out = subprocess.run(["nm", "-D", "--defined-only", ceilings.CEILINGS_PATH], capture_output=True, text=True).stdout
     assert set(syms) <= set(re.findall(r" T (dgc_[a-z0-9_]+)", out))
     lib = ceilings.load()
@@ -164,6 +164,8 @@ def test_ceilings_library_exports_every_declared_symbol():
     assert lib.dgc_mfma(0, 1, 0, ctypes.c_void_p(0x1000), None) == -1
     assert lib.dgc_chase(ctypes.c_void_p(0x1000), 10, 3, ctypes.c_void_p(0x1000), None) == -1
     assert lib.dgc_chase(None, 10, 0, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.dgc_fill(ctypes.c_void_p(0x1000), 65536, 2, 8, ctypes.c_void_p(0x1000), None) == -1   # steps overflow
+    assert lib.dgc_fill(ctypes.c_void_p(0x1000), 65536, 1, 3, ctypes.c_void_p(0x1000), None) == -1   # share must divide 32
 
 
 def test_layout_check_on_host(lib):
