@@ -35,6 +35,8 @@ struct Params {
                            // 4 = B packed FP4 (E2M1) with E8M0 scales, sfb int32 [K/128][N]
   int sk_splits;           // tile kernels: > 1 splits each XCD's tail items over K into this many parts
   int sk_tail;             // tail items per XCD reserved in the workspace (partial index stride)
+  int k_window;            // tile kernels: K blocks taken in aligned windows of this many (a power of
+                           // two; <= 1 = in order), each tile at its own offset in every window
   float* d32;              // K-grouped: fp32 D [G][M][N]
   const float* c32;        // K-grouped: fp32 C [G][M][N] or nullptr
 };

@@ -28,6 +28,10 @@
 //     same XCD and meet in its L2; the items of a last, partial round may be
 //     split over K (the split tail: fp32 partials that a reduction kernel
 //     sums);
+//   * dense and K-grouped items take their K blocks in aligned windows of
+//     p.k_window blocks, each tile starting at its own offset inside every
+//     window, so that the tiles of an XCD that share A rows or B columns do
+//     not all request the same K block at the same time;
 //   * masked form: each workgroup builds the per-group tile counts from the
 //     device-resident masked_m in LDS and walks the expert groups, skipping
 //     empty ones; contiguous form: the expert of each 128-row block is read
@@ -684,8 +688,21 @@ fp8_gemm_nt_kernel(PT p) {
     // K-grouped: this wave's 64 column scales of each K block
     const float* sc_src = SB + min(n0 + 64 * (wave % (BN / 64)) + lane, p.N - 1);
 
-    // the k-th load instruction (k < LPS) of K block i into slot u
+    // K order: with a window of W = p.k_window blocks (a power of two), the
+    // blocks of each aligned window are taken starting at offset (mt + nt) mod W
+    // of that window; blocks after the last whole window stay in order.  Tiles
+    // next to each other in a round then fetch different blocks of a window at
+    // the same time, and each finds the blocks its neighbours fetched earlier in
+    // the L2.  The summation order depends on the tile's position alone, so
+    // results are the same from call to call.
+    const int kwm0 = p.k_window > 1 ? p.k_window - 1 : 0;
+    const int kwm = (kwm0 & (kwm0 + 1)) == 0 ? kwm0 : 0;       // window mask (in order unless W = 2^n)
+    const int kwin = __builtin_amdgcn_readfirstlane((mt + nt) & kwm);
+    const int kfull = kbs & ~kwm;                                // blocks in whole windows
+
+    // the k-th load instruction (k < LPS) of the item's i-th K block into slot u
     auto issue_one = [&](int k, int i, int u) {
+      i = __builtin_amdgcn_readfirstlane(i < kfull ? (i & ~kwm) | ((i + kwin) & kwm) : i);
       if (S::HAS_CS && k == S::LPS - 1) {
         dma_4(sc_src + (size_t)i * p.N, smem_base + S::SC_REGION + u * S::SC_BYTES + wave * 256);
       } else if (k < S::A_INSTR) {

@@ -10,7 +10,8 @@ dense calls.
   element stays bit-identical (the kernels sum in a fixed order).
 * A grouped call equals, row for row and bit for bit, dense calls on each
   expert's rows with that expert's B when both run the same tile kernel
-  (forced configuration, no split tail): the grouping only selects operands.
+  (forced configuration, no split tail, K blocks in order): the grouping only
+  selects operands.
 
 The scale layouts follow the DeepGEMM pages (fine-grained scaling: one scale
 per row per 128 K values for A, per 128x128 block for B)."""
@@ -151,6 +152,7 @@ def test_contiguous_equals_per_expert_dense(dg, monkeypatch, cfg):
     log(f"case: contiguous vs per-expert dense calls, config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_SK_SPLITS", "0")
+    monkeypatch.setenv("DG_K_WINDOW", "1")      # the dense calls in the M-grouped forms' K order
     p = inputgen.make_contiguous(5, 384, 1024, 900, seed=8)
     got = call(dg, p)
     for g in range(p.G):
@@ -166,6 +168,7 @@ def test_masked_equals_per_expert_dense(dg, monkeypatch, cfg):
     log(f"case: masked vs per-expert dense calls, config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_SK_SPLITS", "0")
+    monkeypatch.setenv("DG_K_WINDOW", "1")      # the dense calls in the M-grouped forms' K order
     p = inputgen.make_masked(5, 320, 512, 768, seed=9, masked_m=[0, 320, 1, 129, 255])
     got = call(dg, p)
     for g in range(p.G):

@@ -71,6 +71,16 @@ def test_kgrouped_every_tile_config_exact(dg, monkeypatch, cfg):
     assert np.array_equal(got.view(np.uint32), oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c).view(np.uint32))
 
 
+@pytest.mark.parametrize("window", ["1", "4", "16"])
+def test_kgrouped_k_window_orders(dg, monkeypatch, window):
+    # the K order inside each group's range: groups of 1 to 9 K blocks
+    log(f"case: k-grouped exact, K window {window}")
+    monkeypatch.setenv("DG_K_WINDOW", window)
+    p = inputgen.exact_kgrouped(5, 528, 400, [128, 512, 1152, 640, 0], seed=5)
+    got = run_kg(dg, p)
+    assert np.array_equal(got.view(np.uint32), oracle.k_grouped_tn(p.a, p.sfa, p.b, p.sfb, p.ks, p.c).view(np.uint32))
+
+
 def test_kgrouped_without_c_and_in_place(dg):
     log("case: k-grouped without C, then accumulating into C in place")
     p = inputgen.exact_kgrouped(3, 64, 128, [128, 256, 0], seed=3)

@@ -136,6 +136,25 @@ def test_dense_k_zero_gives_c(dg):
     del a, b, sfa, sfb
 
 
+@pytest.mark.parametrize("window", ["1", "2", "4", "8", "16"])
+def test_dense_k_window_orders(dg, monkeypatch, window):
+    # every K order of the tile kernels sums the same blocks, so the exact
+    # regime stays bit for bit: K block counts below, at and past whole
+    # windows, several tiles (each starts at its own offset in a window), and
+    # the split tail (each split orders its own range)
+    log(f"case: dense K window {window}")
+    monkeypatch.setenv("DG_K_WINDOW", window)
+    for cfg, (M, N, K) in [("11", (512, 512, 13 * 128)), ("6", (384, 768, 16 * 128)),
+                           ("0", (256, 384, 3 * 128)), ("5", (512, 256, 21 * 128))]:
+        monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+        p = inputgen.exact_dense(M, N, K, seed=int(window) + M)
+        assert np.array_equal(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)), (cfg, M, N, K)
+    monkeypatch.setenv("DG_FORCE_CONFIG", "6")
+    monkeypatch.setenv("DG_SK_SPLITS", "3")
+    p = inputgen.exact_dense(1152, 2048, 40 * 128, seed=int(window))
+    assert np.array_equal(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)), "split tail"
+
+
 def test_dense_split_k_forced_matches(dg, monkeypatch):
     log("case: forced split-K")
     monkeypatch.setenv("DG_FORCE_CONFIG", "1")
