@@ -21,7 +21,8 @@
 //     still gives every CU one, counting m-tiles per group; 128x256 rather
 //     than 256x256 when the call has a C; a last partial round of items is
 //     split over K where the tile allows (the split tail); dense and
-//     K-grouped items take their K blocks in windows of 4 (k_window_for);
+//     K-grouped items on the 256x256 tile take their K blocks in windows of 4
+//     (k_window_for);
 //   * the power-of-two kernels (scales applied inside the MFMA) are selected
 //     with DG_FORCE_CONFIG; they run behind a scale check that leaves its
 //     verdicts on the device, beside the general kernel, and exactly one of
@@ -186,15 +187,19 @@ int env_int(const char* name, int dflt) {
 }
 
 // K-block window of the tile kernels (Params::k_window).  Dense and K-grouped
-// items take their K blocks in windows of 4, each tile at its own offset in
-// the window: measured 2% faster on the 4096x7168x16384 NT prefill problem,
-// 5-7% with K-major operands and on the K-grouped problem.  The M-grouped
-// forms keep the plain order (measured no faster, contiguous 1% slower).
-// DG_K_WINDOW overrides the window (1 = plain order; a power of two up to 16).
-int k_window_for(int mode) {
+// items on the 256x256 tile take their K blocks in windows of 4, each tile at
+// its own offset in the window: measured 2% faster on the 4096x7168x16384 NT
+// prefill problem, 5-7% with K-major operands and on the K-grouped problem,
+// 4-5% at 2048x7168x7168 and 8192^3.  The smaller tiles keep the plain order
+// (128x128 measured 2-4% slower with windows, 128x256 within 1.3% either way),
+// and so do the M-grouped forms (contiguous 1% slower, masked no faster).
+// DG_K_WINDOW sets the window of every dense and K-grouped tile (1 = plain
+// order; a power of two up to 16).
+int k_window_for(int mode, int cfg) {
   if (mode != dg::kDense && mode != dg::kKGrouped) return 1;
-  const int w = env_int("DG_K_WINDOW", 4);
-  return w >= 1 && w <= 16 && (w & (w - 1)) == 0 ? w : 4;
+  const int w = env_int("DG_K_WINDOW", 0);
+  if (w >= 1 && w <= 16 && (w & (w - 1)) == 0) return w;
+  return cfg == dg::kCfg256x256w8 ? 4 : 1;
 }
 
 // The decode kernel runs one workgroup per CU; with a long K its splits (at
@@ -438,7 +443,7 @@ int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, cons
   if (grid == 0) return DG_ERR_UNSUPPORTED;
   p.sk_splits = 1;
   p.sk_tail = 0;
-  p.k_window = k_window_for(mode);
+  p.k_window = k_window_for(mode, ch.cfg);
   if (ch.gated_cfg < 0 && ch.splits == 1) {
     const int sk_grid = plan_split_tail(mode, ch.cfg, p, r.num_cus, r.ws_bytes);
     if (sk_grid > 0) grid = sk_grid;
@@ -636,7 +641,6 @@ extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* s
   p.K = (int)K;
   p.G = num_groups;
   p.splits = 1;
-  p.k_window = k_window_for(dg::kKGrouped);
   // the tile by rounds of the chip times the rows loaded per K block, as for
   // dense calls; with a C the 256x256 tile is left out: it reads C per element
   // between its stores, while the smaller tiles read it a strip ahead
@@ -651,6 +655,7 @@ extern "C" int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* s
   const int forced = env_int("DG_FORCE_CONFIG", -1);
   if (forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 || forced == dg::kCfg256x256w8) cfg = forced;
   const dg::ConfigInfo& ci = dg::config_info(cfg);
+  p.k_window = k_window_for(dg::kKGrouped, cfg);
   p.tiles_m = (M + ci.bm - 1) / ci.bm;
   p.tiles_n = (N + ci.bn - 1) / ci.bn;
   const long long items = (long long)num_groups * p.tiles_m * p.tiles_n;
