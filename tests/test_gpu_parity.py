@@ -136,12 +136,13 @@ def test_dense_k_zero_gives_c(dg):
     del a, b, sfa, sfb
 
 
-@pytest.mark.parametrize("window", ["1", "2", "4", "8", "16"])
+@pytest.mark.parametrize("window", ["1", "2", "4", "8", "16", "3", "32"])
 def test_dense_k_window_orders(dg, monkeypatch, window):
     # every K order of the tile kernels sums the same blocks, so the exact
     # regime stays bit for bit: K block counts below, at and past whole
     # windows, several tiles (each starts at its own offset in a window), and
-    # the split tail (each split orders its own range)
+    # the split tail (each split orders its own range); a window that is not
+    # a power of two up to 16 falls back to the default order
     log(f"case: dense K window {window}")
     monkeypatch.setenv("DG_K_WINDOW", window)
     for cfg, (M, N, K) in [("11", (512, 512, 13 * 128)), ("6", (384, 768, 16 * 128)),
