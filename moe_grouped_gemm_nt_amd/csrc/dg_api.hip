@@ -61,14 +61,23 @@ int fail(int status, const char* fmt, ...) {
 constexpr int kMaxDevices = 64;
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;    // split-K partial tiles
 
+// Control memory of a call besides its split-K partials: the scale-check
+// verdicts, then the one-launch decode kernel's counters (zero at set-up; every
+// call of that kernel leaves them at zero).
+constexpr size_t kVerdictBytes = 256;
+constexpr size_t kSyncBytes = sizeof(int32_t) * dg::kSyncInts;
+static_assert(dg::kCheckWGs * sizeof(int32_t) <= kVerdictBytes, "verdicts fit their area");
+
 struct DeviceState {
   std::atomic<bool> ready{false};   // set once, with release order, after the fields below
   int num_cus = 0;
   float* workspace = nullptr;
   int32_t* verdicts = nullptr;    // scale check results, dg::kCheckWGs entries
+  int32_t* sync = nullptr;        // dg::kSyncInts counters
 };
 
 DeviceState g_dev[kMaxDevices];
+
 std::mutex g_mu;
 
 int get_device_state(DeviceState** out) {
@@ -89,14 +98,19 @@ int get_device_state(DeviceState** out) {
       int32_t* verdicts = nullptr;
       e = hipMalloc(&ws, kWorkspaceBytes);
       if (e != hipSuccess) return fail(DG_ERR_HIP, "hipMalloc(workspace): %s", hipGetErrorString(e));
-      e = hipMalloc(&verdicts, sizeof(int32_t) * dg::kCheckWGs);
+      e = hipMalloc(&verdicts, kVerdictBytes + kSyncBytes);
+      if (e == hipSuccess) e = hipMemset(verdicts, 0, kVerdictBytes + kSyncBytes);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) {
-        (void)hipFree(ws);   // nothing is kept from a failed set-up; the next call tries again
-        return fail(DG_ERR_HIP, "hipMalloc(verdicts): %s", hipGetErrorString(e));
+        // nothing is kept from a failed set-up; the next call tries again
+        (void)hipFree(ws);
+        if (verdicts) (void)hipFree(verdicts);
+        return fail(DG_ERR_HIP, "control memory set-up: %s", hipGetErrorString(e));
       }
       st.num_cus = prop.multiProcessorCount;
       st.workspace = ws;
       st.verdicts = verdicts;
+      st.sync = verdicts + kVerdictBytes / sizeof(int32_t);
       st.ready.store(true, std::memory_order_release);
     }
   }
@@ -317,12 +331,13 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
   // DG_FORCE_CONFIG picks a configuration; a power-of-two one runs behind the
   // scale check, beside the general 128x128 kernel.
   const int forced = env_int("DG_FORCE_CONFIG", -1);
+  const bool forced_decode = forced == dg::kCfgDecode || forced == dg::kCfgDecodeFused;
   const bool forced_ok = !kmajor || forced == dg::kCfg128x128 || forced == dg::kCfg128x256w8 ||
-                         forced == dg::kCfg256x256w8 || forced == dg::kCfgDecode;
+                         forced == dg::kCfg256x256w8 || forced_decode;
   // (the decode and narrow kernels are dense-only and need a K block: with
   // K = 0 a forced choice of them is ignored)
   if (forced >= 0 && forced < dg::kNumConfigs && forced_ok &&
-      ((forced != dg::kCfgDecode && forced != dg::kCfgNarrow) || (mode == dg::kDense && KB > 0))) {
+      ((!forced_decode && forced != dg::kCfgNarrow) || (mode == dg::kDense && KB > 0))) {
     if (forced == dg::kCfgE8_128x256 || forced == dg::kCfgWs_128x256 || forced == dg::kCfgE8_256x256) {
       ch.cfg = dg::kCfg128x128x2;
       ch.gated_cfg = forced;
@@ -331,14 +346,21 @@ Choice choose(int mode, int rows, int N, int K, int groups, int num_cus, int ab_
       ch.gated_cfg = -1;
     }
   }
-  if (ch.cfg == dg::kCfgDecode || ch.cfg == dg::kCfgNarrow) ch.gated_cfg = -1;
-  if (ch.cfg == dg::kCfgDecode) {
+  const bool is_decode = ch.cfg == dg::kCfgDecode || ch.cfg == dg::kCfgDecodeFused;
+  if (is_decode || ch.cfg == dg::kCfgNarrow) ch.gated_cfg = -1;
+  if (is_decode) {
     const int fs = env_int("DG_FORCE_SPLITS", 0);
     if (fs > 0) ch.splits = fs;
     if (ch.splits < (KB + 7) / 8) ch.splits = (KB + 7) / 8;   // at most 8 K blocks per split
     if (ch.splits > KB) ch.splits = KB > 0 ? KB : 1;
     ch.kbs = (KB + ch.splits - 1) / ch.splits;
     ch.splits = ch.kbs > 0 ? (KB + ch.kbs - 1) / ch.kbs : 1;  // no empty splits
+    // the one-launch form (DG_FORCE_CONFIG 12) needs a counter per tile; it
+    // measured slower than the two launches on the decode shapes (its last
+    // split reduces the whole tile through one CU, where the reduction
+    // kernel spreads it over the chip), so it is not the default
+    const long long tiles64 = ((long long)(rows + 63) / 64) * ((N + 63) / 64);
+    if (ch.cfg == dg::kCfgDecodeFused && tiles64 > dg::kSyncMaxTiles) ch.cfg = dg::kCfgDecode;
   } else {
     ch.splits = 1;
   }
@@ -382,7 +404,7 @@ int plan_split_tail(int mode, int cfg, dg::Params& p, int num_cus, size_t ws_byt
   p.sk_tail = 0;
   if (mode == dg::kMasked || ci.bm * ci.bn > 128 * 256) return 0;
   if (mode == dg::kContiguous && ci.bm > 128) return 0;
-  if (cfg == dg::kCfgDecode || cfg == dg::kCfgNarrow || cfg == dg::kCfgE8_128x256 || cfg == dg::kCfgWs_128x256 ||
+  if (cfg == dg::kCfgDecode || cfg == dg::kCfgDecodeFused || cfg == dg::kCfgNarrow || cfg == dg::kCfgE8_128x256 || cfg == dg::kCfgWs_128x256 ||
       cfg == dg::kCfgE8_256x256)
     return 0;
   const int KB = p.K / 128;
@@ -428,17 +450,21 @@ struct Resources {
   float* workspace;
   size_t ws_bytes;
   int32_t* verdicts;     // dg::kCheckWGs entries
+  int32_t* sync;         // dg::kSyncInts zeroed counters, or nullptr (no one-launch decode)
 };
+
 
 int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, const Resources& r) {
   if ((long long)p.N * 256 * 2 >= (1LL << 31)) return fail(DG_ERR_UNSUPPORTED, "N=%d is too large", p.N);
   Choice ch = choose_call(mode, rows_hint, p.N, p.K, p.G, r.num_cus, p.ab_layout, p.c != nullptr, r.ws_bytes);
-  const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   p.splits = ch.splits;
   p.kbs_per_split = ch.kbs;
   p.workspace = r.workspace;
   p.workspace_bytes = r.ws_bytes;
+  p.sync = r.sync;
+  if (ch.cfg == dg::kCfgDecodeFused && !p.sync) ch.cfg = dg::kCfgDecode;   // no counters: two launches
   p.gate_ok = nullptr;
+  const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   int grid = plan(mode, ch.cfg, p, r.num_cus, ch.gated_cfg >= 0);
   if (grid == 0) return DG_ERR_UNSUPPORTED;
   p.sk_splits = 1;
@@ -481,7 +507,7 @@ int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, cons
 // Caller-supplied workspaces bound to streams (dg_bind_stream_workspace):
 // calls enqueued on a bound stream of that device use it in place of the
 // device's shared workspace.
-constexpr size_t kBoundVerdictBytes = 256;      // the first bytes of a bound workspace hold the verdicts
+constexpr size_t kBoundVerdictBytes = kVerdictBytes;   // the first bytes of a bound workspace hold the verdicts
 struct Binding {
   int dev;
   hipStream_t stream;
@@ -506,13 +532,17 @@ int launch(int mode, dg::Params& p, int rows_hint, hipStream_t stream) {
   DeviceState* st = nullptr;
   int s = get_device_state(&st);
   if (s != DG_OK) return s;
-  Resources r{st->num_cus, st->workspace, kWorkspaceBytes, st->verdicts};
+  Resources r{st->num_cus, st->workspace, kWorkspaceBytes, st->verdicts, st->sync};
   int dev = 0;
   Binding b;
   if (g_nbind.load(std::memory_order_acquire) > 0 && hipGetDevice(&dev) == hipSuccess && find_binding(dev, stream, &b)) {
+    // [verdicts][counters, if the workspace holds more than them][partials]
+    const bool has_sync = b.bytes >= kBoundVerdictBytes + kSyncBytes;
+    const size_t ctl = kBoundVerdictBytes + (has_sync ? kSyncBytes : 0);
     r.verdicts = reinterpret_cast<int32_t*>(b.ptr);
-    r.workspace = reinterpret_cast<float*>(b.ptr + kBoundVerdictBytes);
-    r.ws_bytes = b.bytes - kBoundVerdictBytes;
+    r.sync = has_sync ? reinterpret_cast<int32_t*>(b.ptr + kBoundVerdictBytes) : nullptr;
+    r.workspace = reinterpret_cast<float*>(b.ptr + ctl);
+    r.ws_bytes = b.bytes - ctl;
   }
   return launch_with(mode, p, rows_hint, stream, r);
 }
@@ -780,8 +810,9 @@ extern "C" int dg_choose_config(int form, int rows, int N, int K, int num_groups
 // hipGetSymbolAddress and only that address is handed to kernels.
 namespace dg_noalloc {
 constexpr size_t kScratchBytes = size_t(8) << 20;   // per device, held until the process ends
-constexpr size_t kVerdictBytes = 256;                // dg::kCheckWGs int32 verdicts, padded
-static_assert(dg::kCheckWGs * sizeof(int32_t) <= kVerdictBytes, "verdicts fit their area");
+// [verdicts][one-launch decode counters][partials]; the array starts zeroed
+// (static storage) and every call leaves the counters at zero
+constexpr size_t kCtlBytes = kVerdictBytes + kSyncBytes;
 __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 struct State {
@@ -840,8 +871,9 @@ extern "C" int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const voi
   p.G = 1;
   // the chooser keeps split-K partials within the scratch; a configuration
   // forced beyond it (DG_FORCE_SPLITS) is refused with DG_ERR_UNSUPPORTED
-  const Resources r{st->num_cus, reinterpret_cast<float*>(st->ptr + dg_noalloc::kVerdictBytes),
-                    dg_noalloc::kScratchBytes - dg_noalloc::kVerdictBytes, reinterpret_cast<int32_t*>(st->ptr)};
+  const Resources r{st->num_cus, reinterpret_cast<float*>(st->ptr + dg_noalloc::kCtlBytes),
+                    dg_noalloc::kScratchBytes - dg_noalloc::kCtlBytes, reinterpret_cast<int32_t*>(st->ptr),
+                    reinterpret_cast<int32_t*>(st->ptr + kVerdictBytes)};
   return launch_with(dg::kDense, p, M, static_cast<hipStream_t>(stream), r);
 }
 
@@ -855,6 +887,12 @@ extern "C" int dg_bind_stream_workspace(void* stream, void* workspace, size_t by
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (workspace && bytes >= kBoundVerdictBytes + kSyncBytes) {
+    // the one-launch decode kernel's counters start at zero
+    e = hipMemset(static_cast<uint8_t*>(workspace) + kBoundVerdictBytes, 0, kSyncBytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "clearing the workspace's counters: %s", hipGetErrorString(e));
+  }
   std::lock_guard<std::mutex> lock(g_bind_mu);
   for (size_t i = 0; i < g_bindings.size(); ++i)
     if (g_bindings[i].dev == dev && g_bindings[i].stream == st) {

@@ -39,7 +39,13 @@ struct Params {
                            // two; <= 1 = in order), each tile at its own offset in every window
   float* d32;              // K-grouped: fp32 D [G][M][N]
   const float* c32;        // K-grouped: fp32 C [G][M][N] or nullptr
+  int* sync;               // one-launch decode: kSyncInts counters, zero before and after every call
 };
+
+// Counters of the one-launch decode kernel: 16 reserved, then one per 64x64
+// tile.
+constexpr int kSyncInts = 1024;
+constexpr int kSyncMaxTiles = kSyncInts - 16;
 
 // The K-grouped form carries its groups' K offsets in the launch arguments,
 // so a captured graph replays with the offsets of the captured call.
@@ -62,6 +68,7 @@ enum Config : int {
   kCfgNarrow = 9,     // dense only: 16x48 tile over the whole K, per-wave LDS rings, no split-K
   kCfgE8_256x256 = 10, // power-of-two scales only: 256x256 tile, 8 waves of 128x64, 2-slot ring
   kCfg256x256w8 = 11, // 256x256 tile, 8 waves of 128x64, 2-slot ring (fp32 promotion)
+  kCfgDecodeFused = 12, // dense only: the decode tile with the split-K hand-off inside the launch
   kNumConfigs
 };
 

@@ -123,15 +123,17 @@ __device__ __forceinline__ void mma_block_kmajor(const uint8_t* a_rows, uint32_t
 // LAYOUT: 0 nt; 1 tt (A stored [K][M]); 2 nn (B stored [K][N]); 3 tn (both);
 // 4 FP8 x FP4: B holds packed FP4 (E2M1) codes with E8M0 scales per column per
 // 32 K values, packed four to an int32 [K/128][N].
+// One work item of the decode kernels: the (tile, split) pair's fp32 result
+// over its K blocks, summed over the four waves; on return out[j] holds
+// sub-tile wave*DTPW + j (lane layout of the MFMA result) and the slot memory
+// is free once the workgroup has passed a barrier.
 template <int LAYOUT>
-__global__ void __launch_bounds__(64 * DNW)
-fp8_gemm_nt_decode_kernel(Params p) {
+__device__ __forceinline__ void decode_item(const Params& p, uint8_t* smem, int tile, int split, v4f (&out)[DTPW]) {
   constexpr bool B4 = LAYOUT == 4;
   constexpr bool TA = !B4 && (LAYOUT & 1), TB = !B4 && (LAYOUT & 2);
   constexpr int SM = DBM / 16, SN = DBN / 16, T = DT;
   constexpr int SLOT = dslot<B4>(), LPB = dlpb<B4>();
   constexpr int BROW = B4 ? KBLK / 2 : KBLK;       // bytes of a B row per K block
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,14 +141,6 @@ fp8_gemm_nt_decode_kernel(Params p) {
   const uint32_t smem_base = lds_u32(smem);
   const int KB = p.K / KBLK;
   const int NB = (p.N + 127) / 128;
-
-  // work item: XCD-contiguous ranges of (tile, split), splits of a tile adjacent
-  const int total = p.tiles_m * p.tiles_n * p.splits;
-  const int per_xcd = (total + 7) / 8;
-  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (blockIdx.x / 8 >= per_xcd || w >= total) return;
-  const int tile = w / p.splits;
-  const int split = w % p.splits;
   int mt, nt;
   tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
   const int m0 = mt * DBM, n0 = nt * DBN;
@@ -224,7 +218,7 @@ fp8_gemm_nt_decode_kernel(Params p) {
   for (int i = 0; i < SM; ++i)
 #pragma unroll
     for (int j = 0; j < SN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  const int g16 = lane >> 4, r16 = lane & 15;
+  const int g16 = lane >> 4;
 #pragma unroll
   for (int j = 0; j < DNPW; ++j) {
     if (j < nown) {
@@ -254,41 +248,193 @@ fp8_gemm_nt_decode_kernel(Params p) {
 #pragma unroll
   for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t / SN][t % SN];
   __syncthreads();
-  v4f out[DTPW];
-  int orow[DTPW], ocol[DTPW];                     // this lane's first row and its column
 #pragma unroll
   for (int j = 0; j < DTPW; ++j) {
     const int t = wave * DTPW + j;
     out[j] = red[t * 64 + lane];
 #pragma unroll
     for (int src = 1; src < DNW; ++src) out[j] += red[(src * T + t) * 64 + lane];
-    orow[j] = m0 + (t / SN) * 16 + g16 * 4;
-    ocol[j] = n0 + (t % SN) * 16 + r16;
   }
+}
 
+// The lane's C values of sub-tiles wave*DTPW + j of tile (mt, nt) (zeros
+// without a C).  One branch for the whole set, so that all the loads are in
+// flight together (a branch per element would wait for each load).
+__device__ __forceinline__ void load_c_tile(const Params& p, int mt, int nt, float (&cv)[DTPW][4]) {
+  constexpr int SN = DBN / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4, r16 = lane & 15;
+  if (p.c) {
+#pragma unroll
+    for (int j = 0; j < DTPW; ++j) {
+      const int t = wave * DTPW + j;
+      const int row0 = mt * DBM + (t / SN) * 16 + g16 * 4, col = min(nt * DBN + (t % SN) * 16 + r16, p.N - 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cv[j][e] = bf16_to_f32(p.c[(size_t)min(row0 + e, p.rows - 1) * p.N + col]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < DTPW; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cv[j][e] = 0.f;
+  }
+}
+
+// + C, round to bf16, store: the lane's sub-tiles wave*DTPW + j of `tile`
+__device__ __forceinline__ void decode_store(const Params& p, int tile, const v4f (&res)[DTPW]) {
+  constexpr int SN = DBN / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4, r16 = lane & 15;
+  int mt, nt;
+  tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
+  float cv[DTPW][4];
+  load_c_tile(p, mt, nt, cv);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < DTPW; ++j) {
+      const int t = wave * DTPW + j;
+      const int row = mt * DBM + (t / SN) * 16 + g16 * 4 + e, col = nt * DBN + (t % SN) * 16 + r16;
+      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(res[j][e] + cv[j][e]);
+    }
+}
+
+template <int LAYOUT>
+__global__ void __launch_bounds__(64 * DNW)
+fp8_gemm_nt_decode_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * dslot<LAYOUT == 4>()];
+  // work item: XCD-contiguous ranges of (tile, split), splits of a tile adjacent
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  const int per_xcd = (total + 7) / 8;
+  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (blockIdx.x / 8 >= per_xcd || w >= total) return;
+  const int tile = w / p.splits;
+  const int split = w % p.splits;
+  v4f out[DTPW];
+  decode_item<LAYOUT>(p, smem, tile, split, out);
   if (p.splits > 1) {
     // fp32 partial, in the result layout [tile][split][sub-tile][lane];
     // splitk_reduce_kernel, launched next on the same stream, sums the splits
-    v4f* ws = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (T * 64);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    v4f* ws = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (DT * 64);
 #pragma unroll
     for (int j = 0; j < DTPW; ++j) __builtin_nontemporal_store(out[j], &ws[(wave * DTPW + j) * 64 + lane]);
     return;
   }
-  // single split: + C, round, store
+  decode_store(p, tile, out);   // single split
+}
+
+// ---- one-launch decode: the split-K hand-off inside the launch ------------
+// The splits of a tile hand their fp32 partials to the split that finishes
+// last, inside the one launch; no workgroup waits for another.
+//   * Work items (tile, split) are dealt to the workgroups as in the two-launch
+//     form (XCD-contiguous ranges, the splits of a tile adjacent).
+//   * Each split stores its partial with device-coherent 16-byte stores
+//     (written through to memory), waits until they are complete and counts
+//     itself in on the tile's counter (device-scope atomic); whichever split
+//     sees the count reach the tile's split count reads the other partials
+//     with device-coherent loads, so the hand-off holds wherever the splits
+//     ran.  It sums the splits in split order, as splitk_reduce_kernel does
+//     (bit-identical results), adds C, rounds, stores, and resets the counter.
+// p.sync holds one counter per tile from kSyncTile0 on; every call leaves
+// them at zero.
+constexpr int kSyncTile0 = 16;
+constexpr int kCoherent = 16;     // buffer-access cache policy: SC1 (device scope)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int atomic_add_dev(int* a, int v) {
+  return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(int* a, int v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publishes this split's partial and, for the tile's last split, completes
+// the tile.  Ends with a workgroup barrier.
+__device__ __forceinline__ void decode_hand_off(const Params& p, int tile, int split, const v4f (&out)[DTPW],
+                                                int* s_flag) {
+  constexpr int MAXS = 8;                        // partials loaded per pass
+  constexpr int SN = DBN / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ws_bytes = p.workspace_bytes < 0xFFFFFFF0u ? (uint32_t)p.workspace_bytes : 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(p.workspace, 0, ws_bytes, 0x00020000);
+  // byte offsets: partial [tile][split][sub-tile][lane] of 16 bytes
+  const uint32_t lane_off = (uint32_t)(((wave * DTPW) * 64 + lane) * 16);
+  const uint32_t tile_off = (uint32_t)tile * (uint32_t)p.splits * (uint32_t)(DT * 64 * 16);
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int j = 0; j < DTPW; ++j)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, out[j]), ws,
+                                           tile_off + (uint32_t)split * (DT * 64 * 16) + lane_off + j * 64 * 16, 0,
+                                           kCoherent);
+  // the stores are complete before the workgroup counts itself in
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* cnt = p.sync + kSyncTile0 + tile;
+  if (tid == 0) *s_flag = atomic_add_dev(cnt, 1) == p.splits - 1;
+  __syncthreads();
+  if (*s_flag != 0) {
+    // every other split has stored its partial.  C first, then the partials
+    // in split order, all in flight together
+    int mt, nt;
+    tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
+    const int g16 = lane >> 4, r16 = lane & 15;
+    float cv[DTPW][4];
+    load_c_tile(p, mt, nt, cv);
+    v4f acc[DTPW];
 #pragma unroll
-    for (int j = 0; j < DTPW; ++j) {
-      const int row = orow[j] + e, col = ocol[j];
-      if (p.c) out[j][e] += bf16_to_f32(p.c[(size_t)min(row, p.rows - 1) * p.N + min(col, p.N - 1)]);
+    for (int j = 0; j < DTPW; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < p.splits; s0 += MAXS) {
+      v4f part[MAXS][DTPW];
+#pragma unroll
+      for (int u = 0; u < MAXS; ++u) {
+        const int s = s0 + u;
+        if (s < p.splits && s != split)
+#pragma unroll
+          for (int j = 0; j < DTPW; ++j)
+            part[u][j] = __builtin_bit_cast(
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                         ws, tile_off + (uint32_t)s * (DT * 64 * 16) + lane_off + j * 64 * 16, 0, kCoherent));
+      }
+#pragma unroll
+      for (int u = 0; u < MAXS; ++u) {
+        const int s = s0 + u;
+        if (s < p.splits)
+#pragma unroll
+          for (int j = 0; j < DTPW; ++j) acc[j] += s == split ? out[j] : part[u][j];
+      }
     }
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
     for (int j = 0; j < DTPW; ++j) {
-      const int row = orow[j] + e, col = ocol[j];
-      if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(out[j][e]);
+      const int t = wave * DTPW + j;
+      const int row0 = mt * DBM + (t / SN) * 16 + g16 * 4, col = nt * DBN + (t % SN) * 16 + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (row0 + e < p.rows && col < p.N) p.d[(size_t)(row0 + e) * p.N + col] = f32_to_bf16(acc[j][e] + cv[j][e]);
     }
+    if (tid == 0) store_dev(cnt, 0);
+  }
+  __syncthreads();
+}
+
+template <int LAYOUT>
+__global__ void __launch_bounds__(64 * DNW)
+fp8_gemm_nt_decode_fused_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKBS * dslot<LAYOUT == 4>()];
+  __shared__ int s_flag;
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  const int per_xcd = (total + 7) / 8;
+  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (blockIdx.x / 8 >= per_xcd || w >= total) return;
+  const int tile = w / p.splits;
+  const int split = w % p.splits;
+  v4f out[DTPW];
+  decode_item<LAYOUT>(p, smem, tile, split, out);
+  decode_hand_off(p, tile, split, out, &s_flag);
 }
 
 // Split-K reduction of the decode kernel's partials: one 64-lane workgroup per
@@ -309,10 +455,11 @@ splitk_reduce_kernel(Params p) {
   const int col = nt * DBN + (t % SN) * 16 + r16;
   const v4f* ws = reinterpret_cast<const v4f*>(p.workspace) + (size_t)tile * p.splits * (T * 64) + t * 64 + lane;
 
-  float cv[4];
+  float cv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.c) {   // one branch for the four loads, so that they are in flight together
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    cv[e] = p.c ? bf16_to_f32(p.c[(size_t)min(row0 + e, p.rows - 1) * p.N + min(col, p.N - 1)]) : 0.f;
+    for (int e = 0; e < 4; ++e) cv[e] = bf16_to_f32(p.c[(size_t)min(row0 + e, p.rows - 1) * p.N + min(col, p.N - 1)]);
+  }
   v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.splits; s0 += MAXS) {
     v4f part[MAXS];
@@ -353,18 +500,30 @@ splitk_tile_reduce_kernel(Params p, int bm, int bn, int slots, int contiguous) {
   const int e0 = c * 1024 + threadIdx.x * 4;
   const int row = mt * bm + e0 / bn, col = nt * bn + e0 % bn;
   if (row >= p.rows) return;
-  if (contiguous) {
-    const int g = p.layout[row];
-    if (g < 0 || g >= p.G) return;
-  }
+  // every load (the row's expert id, the partials, C) is issued before the
+  // first is used, so one memory round trip covers them all; then the
+  // partials are summed in split order (deterministic), C added, and the
+  // stores follow (a load after a store would wait for the store too)
+  constexpr int MAXS = 16;                       // split count bound of the split tail
+  const int g = contiguous ? p.layout[row] : 0;
   const v4f* part = reinterpret_cast<const v4f*>(p.workspace + ((size_t)(x * p.sk_tail + t) * p.sk_splits) * bm * bn + e0);
-  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.sk_splits; ++s0) acc += __builtin_nontemporal_load(part + (size_t)s0 * (bm * bn / 4));
-  // C first, then the stores (a load after a store waits for the store too)
+  v4f pv[MAXS];
+#pragma unroll
+  for (int s0 = 0; s0 < MAXS; ++s0)
+    if (s0 < p.sk_splits) pv[s0] = __builtin_nontemporal_load(part + (size_t)s0 * (bm * bn / 4));
+  float cv[4] = {0.f, 0.f, 0.f, 0.f};
   if (p.c) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (col + k < p.N) acc[k] += bf16_to_f32(p.c[(size_t)row * p.N + col + k]);
+    for (int k = 0; k < 4; ++k) cv[k] = bf16_to_f32(p.c[(size_t)row * p.N + min(col + k, p.N - 1)]);
+  }
+  if (contiguous && (g < 0 || g >= p.G)) return;
+  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < MAXS; ++s0)
+    if (s0 < p.sk_splits) acc += pv[s0];
+  if (p.c) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += cv[k];
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -605,6 +764,21 @@ hipError_t launch_decode(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_decode_fused(const Params& p, hipStream_t stream) {
+  if (!p.sync || p.tiles_m * p.tiles_n > kSyncMaxTiles) return hipErrorInvalidValue;
+  const int items = p.tiles_m * p.tiles_n * p.splits;
+  const int grid = ((items + 7) / 8) * 8;
+  switch (p.ab_layout) {
+    case 0: hipLaunchKernelGGL(fp8_gemm_nt_decode_fused_kernel<0>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(fp8_gemm_nt_decode_fused_kernel<1>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(fp8_gemm_nt_decode_fused_kernel<2>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(fp8_gemm_nt_decode_fused_kernel<3>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(fp8_gemm_nt_decode_fused_kernel<4>, dim3(grid), dim3(64 * DNW), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 const ConfigInfo kConfigs[kNumConfigs] = {
     {128, 128, 256, "128x128_w2x2_s4"},
     {DBM, DBN, 64 * DNW, "decode_64x64_ksplit"},
@@ -618,6 +792,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     {NWM, NWN, 256, "narrow_16x48_fullk"},
     {256, 256, 512, "e8m0_256x256_w2x4_s2"},
     {256, 256, 512, "256x256_w2x4_s2"},
+    {DBM, DBN, 64 * DNW, "decode_64x64_ksplit_one_launch"},
 };
 
 }  // namespace
@@ -654,6 +829,7 @@ hipError_t launch_gemm(int mode, int cfg, const Params& p, int grid, hipStream_t
   switch (cfg) {
     case kCfg128x128: return launch_cfg<128, 128, 2, 2, 4>(mode, p, grid, stream);
     case kCfgDecode: return mode == kDense ? launch_decode(p, stream) : hipErrorInvalidValue;
+    case kCfgDecodeFused: return mode == kDense ? launch_decode_fused(p, stream) : hipErrorInvalidValue;
     case kCfg128x64: return launch_cfg<128, 64, 2, 2, 4>(mode, p, grid, stream);
     case kCfg64x128: return launch_cfg<64, 128, 1, 4, 4>(mode, p, grid, stream);
     case kCfg128x128x2: return launch_cfg<128, 128, 2, 2, 2, 2>(mode, p, grid, stream);

@@ -3,8 +3,9 @@ code only, no device): the benchmark's workloads get the kernels their
 measurements favour, and the forced-configuration switch acts as on the calls.
 
 Configuration ids: 0 128x128, 1 decode (64x64 tiles, K split over
-workgroups), 5 256x128, 6 128x256, 7 128x256 with power-of-two scales in the
-MFMA, 9 narrow (16x48 over the whole K), 11 256x256."""
+workgroups, a reduction launch), 5 256x128, 6 128x256, 7 128x256 with
+power-of-two scales in the MFMA, 9 narrow (16x48 over the whole K), 11 256x256,
+12 decode with the splits' hand-off inside one launch."""
 import pytest
 
 import moe_grouped_gemm_nt_amd as dg
@@ -64,6 +65,11 @@ def test_forced_configuration(monkeypatch):
     assert dg.dg_choose_config("dense", 64, 2112, 7168) == (1, 7)
     monkeypatch.setenv("DG_FORCE_SPLITS", "14")
     assert dg.dg_choose_config("dense", 64, 2112, 7168) == (1, 14)
+    monkeypatch.setenv("DG_FORCE_CONFIG", "12")         # the one-launch decode: dense only
+    assert dg.dg_choose_config("dense", 64, 2112, 7168) == (12, 14)
+    assert dg.dg_choose_config("dense", 512, 4096, 7168)[0] == 12
+    assert dg.dg_choose_config("dense", 4096, 4096, 7168)[0] == 1    # 4096 tiles: more than its counters
+    assert dg.dg_choose_config("contiguous", 4096, 7168, 16384)[0] == 6
 
 
 @pytest.mark.parametrize("args", [
@@ -78,7 +84,7 @@ def test_invalid_query(args):
 def test_forced_decode_or_narrow_ignored_without_k_blocks(monkeypatch):
     # K = 0 gives D = C; the decode and narrow kernels index their first K
     # block's scales, so a forced choice of them is ignored there
-    for forced in ("1", "9"):
+    for forced in ("1", "9", "12"):
         monkeypatch.setenv("DG_FORCE_CONFIG", forced)
-        assert dg.dg_choose_config("dense", 64, 2112, 0)[0] not in (1, 9)
+        assert dg.dg_choose_config("dense", 64, 2112, 0)[0] not in (1, 9, 12)
         assert dg.dg_choose_config("dense", 64, 2112, 128)[0] == int(forced)

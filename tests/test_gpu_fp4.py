@@ -59,14 +59,15 @@ def test_fp4_split_tail_exact(dg, monkeypatch, cfg, sk):
     assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))
 
 
+@pytest.mark.parametrize("cfg", ["1", "12"])
 @pytest.mark.parametrize("splits", ["1", "3", "16"])
 @pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (100, 200, 2048), (1, 64, 128)])
-def test_fp4_decode_splits_exact(dg, monkeypatch, splits, M, N, K):
+def test_fp4_decode_splits_exact(dg, monkeypatch, cfg, splits, M, N, K):
     # the decode kernel (64x64 tiles, K split over workgroups) with a forced
     # split count: one split writes the result itself, more go through the
-    # fp32 partials and the split-K reduction
-    log(f"case: fp8 x fp4 decode exact {M}x{N}x{K}, forced splits {splits}")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+    # fp32 partials and the split-K reduction (1) or the in-launch hand-off (12)
+    log(f"case: fp8 x fp4 decode exact {M}x{N}x{K}, config {cfg}, forced splits {splits}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_FORCE_SPLITS", splits)
     p = inputgen.exact_dense_fp4(M, N, K, seed=M + 7)
     assert np.array_equal(run_fp4(dg, p), oracle.gemm_fp8_fp4_nt(p.a, p.sfa, p.b, p.sfb, p.c))

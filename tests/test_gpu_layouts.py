@@ -128,15 +128,17 @@ def test_layout_decode_shape_random_tolerance(dg, layout):
     check_tolerance(got, oracle.gemm_layout(layout, a, p.sfa, b, p.sfb, p.c), layout)
 
 
+@pytest.mark.parametrize("cfg", ["1", "12"])
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
 @pytest.mark.parametrize("splits", ["1", "3", "16"])
 @pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (96, 160, 2048), (16, 16, 128)])
-def test_layout_decode_kernel_exact(dg, monkeypatch, layout, splits, M, N, K):
+def test_layout_decode_kernel_exact(dg, monkeypatch, cfg, layout, splits, M, N, K):
     # the decode kernel (64x64 tiles, K split over workgroups) with K-major
     # operands staged in octets and read with transposing LDS reads; one split
-    # writes D itself, more go through the fp32 partials and the reduction
-    log(f"case: {layout} decode kernel exact {M}x{N}x{K}, forced splits {splits}")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+    # writes D itself, more go through the fp32 partials and the reduction (1)
+    # or the in-launch hand-off (12)
+    log(f"case: {layout} decode kernel exact {M}x{N}x{K}, config {cfg}, forced splits {splits}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     monkeypatch.setenv("DG_FORCE_SPLITS", splits)
     p = inputgen.exact_dense(M, N, K, seed=M + K)
     got, a, b = run_layout(dg, layout, p)
@@ -144,7 +146,7 @@ def test_layout_decode_kernel_exact(dg, monkeypatch, layout, splits, M, N, K):
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
-@pytest.mark.parametrize("cfg", ["1", "0", "11"])
+@pytest.mark.parametrize("cfg", ["1", "12", "0", "11"])
 def test_layout_in_place_c_equals_d(dg, monkeypatch, layout, cfg):
     log(f"case: {layout} in place (c == d), forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

@@ -156,9 +156,15 @@ def test_dense_k_window_orders(dg, monkeypatch, window):
     assert np.array_equal(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)), "split tail"
 
 
-def test_dense_split_k_forced_matches(dg, monkeypatch):
-    log("case: forced split-K")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+# decode configurations: 1 = partials, then the reduction kernel; 12 = one
+# launch, the tile's last split summing the others' device-coherent partials
+DECODE_CFGS = ["1", "12"]
+
+
+@pytest.mark.parametrize("cfg", DECODE_CFGS)
+def test_dense_split_k_forced_matches(dg, monkeypatch, cfg):
+    log(f"case: forced split-K, config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     p = inputgen.exact_dense(64, 640, 4096, seed=13)
     ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
     for splits in ["1", "2", "3", "8"]:
@@ -168,9 +174,10 @@ def test_dense_split_k_forced_matches(dg, monkeypatch):
     monkeypatch.delenv("DG_FORCE_SPLITS")
 
 
-def test_decode_split_k_exact(dg, monkeypatch):
-    log("case: decode split-K, several split counts")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+@pytest.mark.parametrize("cfg", DECODE_CFGS)
+def test_decode_split_k_exact(dg, monkeypatch, cfg):
+    log(f"case: decode split-K, several split counts, config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     for M, N, K in [(64, 2112, 7168), (17, 200, 2048), (100, 640, 4096)]:
         p = inputgen.exact_dense(M, N, K, seed=M + K)
         ref = oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)
@@ -181,9 +188,10 @@ def test_decode_split_k_exact(dg, monkeypatch):
     monkeypatch.delenv("DG_FORCE_SPLITS")
 
 
-def test_decode_split_k_no_stale_partials(dg, monkeypatch):
-    log("case: decode split-K, alternating inputs on one workspace")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+@pytest.mark.parametrize("cfg", DECODE_CFGS)
+def test_decode_split_k_no_stale_partials(dg, monkeypatch, cfg):
+    log(f"case: decode split-K, alternating inputs on one workspace, config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     probs = [inputgen.exact_dense(64, 2112, 7168, seed=s) for s in (40, 41, 42)]
     refs = [oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c) for p in probs]
     devs = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
@@ -196,11 +204,13 @@ def test_decode_split_k_no_stale_partials(dg, monkeypatch):
             assert np.array_equal(bits_host(outs[i]), refs[i]), (rep, i)
 
 
-def test_decode_split_k_graph_replays(dg, monkeypatch):
-    # two launches per call (partials, then their reduction) captured in a
-    # graph and replayed several times, with eager calls between the replays
-    log("case: decode split-K under graph replay")
-    monkeypatch.setenv("DG_FORCE_CONFIG", "1")
+@pytest.mark.parametrize("cfg", DECODE_CFGS)
+def test_decode_split_k_graph_replays(dg, monkeypatch, cfg):
+    # the call's launches (partials, then their reduction; or the one-launch
+    # form with its counters) captured in a graph and replayed several times,
+    # with eager calls between the replays
+    log(f"case: decode split-K under graph replay, config {cfg}")
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     probs = [inputgen.exact_dense(64, 2112, 7168, seed=s) for s in (50, 51)]
     refs = [oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c) for p in probs]
     devs = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
@@ -227,9 +237,20 @@ def test_decode_split_k_graph_replays(dg, monkeypatch):
         assert np.array_equal(bits_host(eager), refs[rep % 2]), rep
 
 
+def test_decode_one_launch_many_tiles(dg, monkeypatch):
+    # the one-launch decode past one round of the chip: 128 tiles in 7 splits
+    # (896 items, 3.5 rounds), 99 tiles in 3 splits, 64 tiles in 2 splits,
+    # then the default shape
+    log("case: one-launch decode, several rounds of items per XCD")
+    monkeypatch.setenv("DG_FORCE_CONFIG", "12")
+    for M, N, K in [(128, 4096, 7168), (130, 2112, 3072), (200, 1000, 1280), (64, 2112, 7168)]:
+        p = inputgen.exact_dense(M, N, K, seed=M + N)
+        assert np.array_equal(run_dense(dg, p), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c)), (M, N, K)
+
+
 # "7", "8" and "10" are the power-of-two-scale kernels, run behind the scale check beside
 # configuration 4: exact inputs take it, the non-power-of-two case must not.
-@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11", "12"])
 def test_dense_every_tile_config(dg, monkeypatch, cfg):
     log(f"case: forced config {cfg}")
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)

@@ -107,7 +107,7 @@ DRIVER = textwrap.dedent(r"""
                         for has_c in (0, 1):
                             expect(ch(form, rows, N, K, 8, 256, lay, has_c, ctypes.byref(cfg), ctypes.byref(spl)), 0,
                                    (form, rows, N, K))
-                            assert 0 <= cfg.value < 12 and spl.value >= 1
+                            assert 0 <= cfg.value < 13 and spl.value >= 1
     expect(ch(3, 8, 8, 128, 1, 256, 0, 0, ctypes.byref(cfg), ctypes.byref(spl)), -1, "bad form")
     expect(ch(0, 8, 8, 128, 1, 256, 0, 0, None, ctypes.byref(spl)), -1, "null out")
     # the layout check
