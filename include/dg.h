@@ -188,9 +188,11 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const void* a, const float* sfa, const v
  * configuration is chosen so that its partials fit the array; one forced
  * beyond it (DG_FORCE_SPLITS) returns DG_ERR_UNSUPPORTED.  Every call on a GPU
  * shares that GPU's array, and nothing in it needs clearing between calls
- * (every call writes what it reads), but calls that may overlap on one GPU
- * (different streams not ordered by events) race on it and must be ordered
- * by the caller.  Returns a dg_status. */
+ * (every call writes what it reads; the one-launch decode configuration's
+ * per-tile counters in it start at zero with the array and every call leaves
+ * them at zero), but calls that may overlap on one GPU (different streams not
+ * ordered by events) race on it and must be ordered by the caller.  Returns a
+ * dg_status. */
 int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const float* sfb,
                            const void* c, void* d, int M, int N, int K, void* stream);
 
@@ -203,7 +205,8 @@ int dg_fp8_gemm_nt_noalloc(const void* a, const float* sfa, const void* b, const
  * the call passes a C.  Writes the configuration id to *cfg (0 128x128 tile,
  * 1 decode kernel with K split over workgroups, 2 128x64, 3 64x128, 4 128x128
  * two per CU, 5 256x128, 6 128x256, 7 and 8 128x256 and 10 256x256 with
- * power-of-two scales in the MFMA, 9 narrow 16x48 whole-K, 11 256x256) and
+ * power-of-two scales in the MFMA, 9 narrow 16x48 whole-K, 11 256x256, 12 the
+ * decode kernel with its splits summed inside the same launch) and
  * the decode kernel's K splits to *splits (1 otherwise).  DG_FORCE_CONFIG and
  * DG_FORCE_SPLITS act as they do on the calls.  Returns DG_ERR_INVALID_ARG
  * for NULL outputs, a form outside 0-2, rows or N below 1, K negative or not
@@ -217,14 +220,18 @@ int dg_choose_config(int form, int rows, int N, int K, int num_groups, int num_c
  * of the device's shared workspace (split-K partial tiles and scale-check
  * verdicts), so that calls running at the same time on different streams no
  * longer share scratch memory.  workspace: device memory on the current
- * device, 256-byte aligned, at least 256 bytes (the verdicts); the rest holds
+ * device, 256-byte aligned, at least 256 bytes (the verdicts).  A workspace of
+ * at least 256 + 4096 bytes also holds, after the verdicts, the 4096 bytes of
+ * counters of the one-launch decode configuration, which this call clears
+ * (synchronously) and every later call leaves at zero; the rest holds
  * partials, and the configuration is chosen so that they fit (a bound
  * workspace of a few hundred bytes simply means no split-K).  The caller keeps
  * the memory alive, and unused by anything else, while the binding lasts and
  * while calls enqueued with it run.  workspace NULL (or bytes 0) removes the
  * stream's binding.  The allocation-free call (dg_fp8_gemm_nt_noalloc) always
  * uses its own fixed array.  Returns DG_ERR_INVALID_ARG for a misaligned or
- * too small workspace, DG_ERR_HIP if the current device cannot be queried. */
+ * too small workspace, DG_ERR_HIP if the current device cannot be queried or
+ * the counters cannot be cleared. */
 int dg_bind_stream_workspace(void* stream, void* workspace, size_t bytes);
 
 /* Host-side check of a contiguous grouped_layout held in HOST memory (M int32
