@@ -462,7 +462,11 @@ int launch_with(int mode, dg::Params& p, int rows_hint, hipStream_t stream, cons
   p.workspace = r.workspace;
   p.workspace_bytes = r.ws_bytes;
   p.sync = r.sync;
-  if (ch.cfg == dg::kCfgDecodeFused && !p.sync) ch.cfg = dg::kCfgDecode;   // no counters: two launches
+  // the one-launch form needs the counters and addresses its partials with
+  // 32-bit offsets; otherwise the two launches
+  if (ch.cfg == dg::kCfgDecodeFused &&
+      (!p.sync || ((long long)(p.rows + 63) / 64) * ((p.N + 63) / 64) * ch.splits * 64 * 64 * 4 >= (1LL << 32)))
+    ch.cfg = dg::kCfgDecode;
   p.gate_ok = nullptr;
   const dg::ConfigInfo& ci = dg::config_info(ch.cfg);
   int grid = plan(mode, ch.cfg, p, r.num_cus, ch.gated_cfg >= 0);

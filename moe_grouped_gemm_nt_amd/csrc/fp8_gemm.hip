@@ -343,6 +343,7 @@ fp8_gemm_nt_decode_kernel(Params p) {
 // them at zero.
 constexpr int kSyncTile0 = 16;
 constexpr int kCoherent = 16;     // buffer-access cache policy: SC1 (device scope)
+constexpr int kRawBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw access
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int atomic_add_dev(int* a, int v) {
@@ -362,8 +363,9 @@ __device__ __forceinline__ void decode_hand_off(const Params& p, int tile, int s
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ws_bytes = p.workspace_bytes < 0xFFFFFFF0u ? (uint32_t)p.workspace_bytes : 0xFFFFFFF0u;
-  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(p.workspace, 0, ws_bytes, 0x00020000);
-  // byte offsets: partial [tile][split][sub-tile][lane] of 16 bytes
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(p.workspace, 0, ws_bytes, kRawBufferWord3);
+  // byte offsets (32-bit: the host keeps every partial below 4 GiB): partial
+  // [tile][split][sub-tile][lane] of 16 bytes
   const uint32_t lane_off = (uint32_t)(((wave * DTPW) * 64 + lane) * 16);
   const uint32_t tile_off = (uint32_t)tile * (uint32_t)p.splits * (uint32_t)(DT * 64 * 16);
 #pragma unroll

@@ -78,3 +78,17 @@ def test_forced_beyond_scratch_is_refused(dg, monkeypatch):
     dg.dg_fp8_gemm_nt(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c), d)
     torch.cuda.synchronize()
     assert np.array_equal(bits_host(d), oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
+
+
+def test_one_launch_decode_counters_left_at_zero(dg, monkeypatch):
+    # the one-launch decode keeps one counter per tile in the scratch array:
+    # they start at zero with the array and every call leaves them there, so
+    # calls in a row (the second on fewer tiles, the third on more) agree with
+    # the allocating call and the oracle bit for bit
+    monkeypatch.setenv("DG_FORCE_CONFIG", "12")
+    for i, (M, N, K) in enumerate([(64, 2112, 7168), (100, 640, 4096), (64, 2112, 7168)]):
+        print(f"case: noalloc one-launch decode {M}x{N}x{K} (call {i + 1} of 3)", flush=True)
+        p = inputgen.exact_dense(M, N, K, seed=95 + i)
+        got, ref_entry = both(dg, p)
+        assert np.array_equal(got, ref_entry)
+        assert np.array_equal(got, oracle.gemm_nt(p.a, p.sfa, p.b, p.sfb, p.c))
