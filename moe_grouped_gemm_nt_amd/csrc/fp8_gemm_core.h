@@ -51,7 +51,11 @@
 //     split the result goes through the +C / bf16 epilogue; otherwise every
 //     split stores its fp32 partial to a workspace and splitk_reduce_kernel,
 //     launched next on the same stream, sums the splits in split order
-//     (deterministic), adds C and rounds; the kernel boundary orders the two.
+//     (deterministic), adds C and rounds; the kernel boundary orders the two;
+//   * fp8_gemm_nt_decode_fused_kernel (opt-in) runs the same items in one
+//     launch: each split publishes its partial with device-coherent stores
+//     and counts itself in on its tile's counter, and the tile's last split
+//     sums the partials in split order and finishes the tile.
 //
 // LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by row so that the
 // fragment reads of a 16-row strip are free of bank conflicts.
