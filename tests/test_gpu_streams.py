@@ -1,7 +1,8 @@
 """Per-stream workspaces (dg_bind_stream_workspace): decode-shape calls that
-split K (fp32 partials in the workspace) enqueued on two streams at once, each
-stream with its own bound workspace, give the oracle's result bit for bit; a
-workspace too small for partials gives the same result without a split."""
+split K (fp32 partials in the workspace, and for the one-launch form its
+per-tile counters) enqueued on two streams at once, each stream with its own
+bound workspace, give the oracle's result bit for bit; a workspace too small
+for partials gives the same result without a split."""
 import numpy as np
 import pytest
 import torch
@@ -22,8 +23,12 @@ def dg():
     return m
 
 
-def test_two_streams_with_their_own_workspaces(dg):
-    print("case: two streams, bound workspaces, 64x2112x7168 split-K calls overlapping", flush=True)
+# 1: partials, then the reduction kernel; 12: one launch, with the per-tile
+# counters in each bound workspace
+@pytest.mark.parametrize("cfg", ["1", "12"])
+def test_two_streams_with_their_own_workspaces(dg, monkeypatch, cfg):
+    print(f"case: two streams, bound workspaces, 64x2112x7168 split-K calls overlapping, config {cfg}", flush=True)
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     probs = [inputgen.exact_dense(64, 2112, 7168, seed=200 + i) for i in range(2)]
     ins = [(dev(p.a), dev(p.sfa), dev(p.b), dev(p.sfb), bf16_bits_dev(p.c)) for p in probs]
     outs = [sentinel_like((64, 2112)) for _ in probs]
