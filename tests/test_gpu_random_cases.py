@@ -41,7 +41,7 @@ def draw_cases(n=160, seed=2026):
         M = max(16, M // 16 * 16) if a_kmajor else M
         N = int(rng.choice([1, 48, 130, 256, 400, 777, 1100, 2112]))
         N = max(16, N // 16 * 16) if b_kmajor else N
-        cfg = rng.choice([None, None, "0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11"])
+        cfg = rng.choice([None, None, "0", "1", "2", "3", "4", "5", "6", "7", "8", "9", "10", "11", "12"])
         env = {}
         if cfg is not None:
             env["DG_FORCE_CONFIG"] = str(cfg)
@@ -50,7 +50,7 @@ def draw_cases(n=160, seed=2026):
             env["DG_SK_SPLITS"] = "0"
         elif r < 0.5:
             env["DG_SK_SPLITS"] = str(int(rng.integers(2, 17)))
-        if cfg == "1" and rng.random() < 0.5:
+        if cfg in ("1", "12") and rng.random() < 0.5:
             env["DG_FORCE_SPLITS"] = str(int(rng.integers(1, 9)))
         case = dict(i=i, form=form, M=M, N=N, K=K, env=env, with_c=bool(rng.random() < 0.5),
                     seed=int(rng.integers(0, 1 << 30)))
