@@ -42,10 +42,11 @@ struct Params {
   int* sync;               // one-launch decode: kSyncInts counters, zero before and after every call
 };
 
-// Counters of the one-launch decode kernel: 16 reserved, then one per 64x64
-// tile.
+// Counters of the one-launch decode kernel: kSyncTile0 reserved, then one per
+// 64x64 tile.
 constexpr int kSyncInts = 1024;
-constexpr int kSyncMaxTiles = kSyncInts - 16;
+constexpr int kSyncTile0 = 16;
+constexpr int kSyncMaxTiles = kSyncInts - kSyncTile0;
 
 // The K-grouped form carries its groups' K offsets in the launch arguments,
 // so a captured graph replays with the offsets of the captured call.

@@ -281,16 +281,14 @@ __device__ __forceinline__ void load_c_tile(const Params& p, int mt, int nt, flo
   }
 }
 
-// + C, round to bf16, store: the lane's sub-tiles wave*DTPW + j of `tile`
-__device__ __forceinline__ void decode_store(const Params& p, int tile, const v4f (&res)[DTPW]) {
+// + C (cv, from load_c_tile), round to bf16, store: the lane's sub-tiles
+// wave*DTPW + j of tile (mt, nt)
+__device__ __forceinline__ void store_d_tile(const Params& p, int mt, int nt, const v4f (&res)[DTPW],
+                                             const float (&cv)[DTPW][4]) {
   constexpr int SN = DBN / 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g16 = lane >> 4, r16 = lane & 15;
-  int mt, nt;
-  tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
-  float cv[DTPW][4];
-  load_c_tile(p, mt, nt, cv);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -299,6 +297,15 @@ __device__ __forceinline__ void decode_store(const Params& p, int tile, const v4
       const int row = mt * DBM + (t / SN) * 16 + g16 * 4 + e, col = nt * DBN + (t % SN) * 16 + r16;
       if (row < p.rows && col < p.N) p.d[(size_t)row * p.N + col] = f32_to_bf16(res[j][e] + cv[j][e]);
     }
+}
+
+// + C, round to bf16, store: the lane's sub-tiles wave*DTPW + j of `tile`
+__device__ __forceinline__ void decode_store(const Params& p, int tile, const v4f (&res)[DTPW]) {
+  int mt, nt;
+  tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
+  float cv[DTPW][4];
+  load_c_tile(p, mt, nt, cv);
+  store_d_tile(p, mt, nt, res, cv);
 }
 
 template <int LAYOUT>
@@ -341,7 +348,6 @@ fp8_gemm_nt_decode_kernel(Params p) {
 //     (bit-identical results), adds C, rounds, stores, and resets the counter.
 // p.sync holds one counter per tile from kSyncTile0 on; every call leaves
 // them at zero.
-constexpr int kSyncTile0 = 16;
 constexpr int kCoherent = 16;     // buffer-access cache policy: SC1 (device scope)
 constexpr int kRawBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw access
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -358,7 +364,6 @@ __device__ __forceinline__ void store_dev(int* a, int v) {
 __device__ __forceinline__ void decode_hand_off(const Params& p, int tile, int split, const v4f (&out)[DTPW],
                                                 int* s_flag) {
   constexpr int MAXS = 8;                        // partials loaded per pass
-  constexpr int SN = DBN / 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,7 +389,6 @@ __device__ __forceinline__ void decode_hand_off(const Params& p, int tile, int s
     // in split order, all in flight together
     int mt, nt;
     tile_coords(tile, p.tiles_m, p.tiles_n, mt, nt);
-    const int g16 = lane >> 4, r16 = lane & 15;
     float cv[DTPW][4];
     load_c_tile(p, mt, nt, cv);
     v4f acc[DTPW];
@@ -410,14 +414,7 @@ __device__ __forceinline__ void decode_hand_off(const Params& p, int tile, int s
           for (int j = 0; j < DTPW; ++j) acc[j] += s == split ? out[j] : part[u][j];
       }
     }
-#pragma unroll
-    for (int j = 0; j < DTPW; ++j) {
-      const int t = wave * DTPW + j;
-      const int row0 = mt * DBM + (t / SN) * 16 + g16 * 4, col = nt * DBN + (t % SN) * 16 + r16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (row0 + e < p.rows && col < p.N) p.d[(size_t)(row0 + e) * p.N + col] = f32_to_bf16(acc[j][e] + cv[j][e]);
-    }
+    store_d_tile(p, mt, nt, acc, cv);
     if (tid == 0) store_dev(cnt, 0);
   }
   __syncthreads();
