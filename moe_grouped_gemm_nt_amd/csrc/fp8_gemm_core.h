@@ -813,8 +813,11 @@ fp8_gemm_nt_kernel(PT p) {
       // issued, so its FMAs need no wait states for the MFMA result and can
       // issue while the matrix core runs the later MFMAs (P = 4 measured 2-4%
       // faster than 2 on the NT and FP4 prefill shapes; the K-major layouts
-      // keep 2, where 4 spills registers)
-      constexpr int P = (LAYOUT == 0 || LAYOUT == 4) ? 4 : 2;
+      // keep 2, where 4 spills registers; the dense nt 256x256 tile, whose
+      // schedule interleaves each MFMA with four FMAs below, takes 3: 0.3-1.2%
+      // faster than 4 there)
+      constexpr bool INTERLEAVED = MODE == kDense && LAYOUT == 0 && !E8M0 && S::SM * S::SN >= 32;
+      constexpr int P = INTERLEAVED ? 3 : (LAYOUT == 0 || LAYOUT == 4) ? 4 : 2;
       v4f part[P];
 #pragma unroll
       for (int t = 0; t < T + P - 1; ++t) {
