@@ -824,12 +824,18 @@ fp8_gemm_nt_kernel(PT p) {
         if (t < T) {
           if (t % S::SN == 0 && t / S::SN + 1 < SMA) {
             // keep the scheduler from hoisting every strip's reads to the top
-            if constexpr (S::SM * S::SN >= 32) {
-              // dense nt and nn: the strip just scheduled issues each MFMA
-              // followed by four promotion FMAs, rather than its FMAs in one
-              // run ahead of its MFMAs (prefill 1.4-1.6% faster; the FP4,
-              // K-major-A and K-grouped kernels measured no gain or a loss)
-              if constexpr (MODE == kDense && (LAYOUT == 0 || LAYOUT == 2) && !E8M0) {
+            // (the 256x256 tile; the eight-wave nt tiles of 64x64 wave tiles
+            // take the same per-strip regions for the hints below)
+            constexpr bool WIDE = S::SM * S::SN >= 32;
+            constexpr bool NT8 = S::NWAVES == 8 && LAYOUT == 0 && !E8M0 && !KG;
+            if constexpr (WIDE || NT8) {
+              // the strip just scheduled issues each MFMA followed by four
+              // promotion FMAs, rather than its FMAs in one run ahead of its
+              // MFMAs: dense nt and nn 256x256 (prefill 1.4-1.6% faster) and the
+              // eight-wave nt 128x256 and 256x128 tiles (contiguous 2-4%
+              // faster, masked unchanged); the FP4, K-major-A and K-grouped
+              // kernels measured no gain or a loss
+              if constexpr (WIDE ? MODE == kDense && (LAYOUT == 0 || LAYOUT == 2) && !E8M0 : NT8) {
                 if (t > 0) {
                   __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next strip's LDS reads
 #pragma unroll
