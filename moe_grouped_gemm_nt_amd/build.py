@@ -25,7 +25,8 @@ SOURCES = {
     "dg_api.hip": [],
 }
 
-# packed fp32 VALU forms are disabled on purpose (see the design notes)
+# packed fp32 VALU forms are disabled on purpose: the kernels issue one fp32
+# operation per VALU instruction, the form their results are tested in
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",

@@ -13,7 +13,7 @@ What is computed (every step in fp64):
     D[m,n] = RNE_bf16( C[m,n] + sum_kb sa[kb,m]
                        * sum_{k in kb} dec8(A[m,k]) * dec4(B[n,k]) * 2**(e[n, k//32] - 127) )
 
-Readings where the pages are silent (listed with the others in the design notes):
+Readings where the pages are silent:
   * FP4 is OCP E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; no
     infinities or NaN; magnitudes 0, 1/2, 1, 3/2, 2, 3, 4, 6.
   * B holds two codes per byte, element 2i in the low nibble, K contiguous:

@@ -28,7 +28,7 @@ significant bits and are multiples of 2**-18; 128 of them stay far below
 precision.  The final rounding goes straight from fp64 to bf16 (never through
 fp32) with round-to-nearest, ties to even.
 
-Readings where the pages are silent (the full list sits in the design notes):
+Readings where the pages are silent:
   * e4m3 is the OCP E4M3FN format: bias 7, no infinities, 0x7F/0xFF are NaN,
     largest finite value 448.
   * A scales are 1x128 (one per row per K block), stored K-block-major
