@@ -308,6 +308,10 @@ __device__ __forceinline__ void decode_store(const Params& p, int tile, const v4
   store_d_tile(p, mt, nt, res, cv);
 }
 
+constexpr int kCoherent = 16;     // buffer-access cache policy: SC1 (device scope)
+constexpr int kRawBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw access
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 template <int LAYOUT>
 __global__ void __launch_bounds__(64 * DNW)
 fp8_gemm_nt_decode_kernel(Params p) {
@@ -323,12 +327,17 @@ fp8_gemm_nt_decode_kernel(Params p) {
   decode_item<LAYOUT>(p, smem, tile, split, out);
   if (p.splits > 1) {
     // fp32 partial, in the result layout [tile][split][sub-tile][lane];
-    // splitk_reduce_kernel, launched next on the same stream, sums the splits
+    // splitk_reduce_kernel, launched next on the same stream, sums the splits.
+    // The stores write through to memory (device-coherent policy), so the
+    // launch ends with no dirty partial lines in the L2s to write back.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    v4f* ws = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (DT * 64);
+    v4f* part = reinterpret_cast<v4f*>(p.workspace) + ((size_t)tile * p.splits + split) * (DT * 64);
+    const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(part, 0, DT * 64 * 16, kRawBufferWord3);
 #pragma unroll
-    for (int j = 0; j < DTPW; ++j) __builtin_nontemporal_store(out[j], &ws[(wave * DTPW + j) * 64 + lane]);
+    for (int j = 0; j < DTPW; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, out[j]), ws,
+                                             (uint32_t)(((wave * DTPW + j) * 64 + lane) * 16), 0, kCoherent);
     return;
   }
   decode_store(p, tile, out);   // single split
@@ -348,9 +357,6 @@ fp8_gemm_nt_decode_kernel(Params p) {
 //     (bit-identical results), adds C, rounds, stores, and resets the counter.
 // p.sync holds one counter per tile from kSyncTile0 on; every call leaves
 // them at zero.
-constexpr int kCoherent = 16;     // buffer-access cache policy: SC1 (device scope)
-constexpr int kRawBufferWord3 = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw access
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int atomic_add_dev(int* a, int v) {
   return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
