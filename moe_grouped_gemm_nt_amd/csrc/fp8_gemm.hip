@@ -156,7 +156,9 @@ __device__ __forceinline__ void decode_item(const Params& p, uint8_t* smem, int 
   for (int j = 0; j < DNPW; ++j)
     sb[j] = B4 || j >= nown ? 1.f : p.sfb[(size_t)nb * KB + kb0 + wave + DNW * j];   // only blocks the wave owns
 
-  // issue every load of this wave's blocks: A (64 rows), B (64 rows), A scales
+  // issue every load of this wave's blocks: A (64 rows), B (64 rows), A scales.
+  // B lines are read once per call (streaming policy); the other column tiles
+  // read A again from the L2 (default policy)
   const int lr = lane >> 3;
 #pragma unroll
   for (int j = 0; j < DNPW; ++j) {
@@ -186,7 +188,7 @@ __device__ __forceinline__ void decode_item(const Params& p, uint8_t* smem, int 
         for (int q = 0; q < DBN / 8; ++q) {
           int kr, c;
           kmajor_slot<DBN>(64 * q + lane, kr, c);
-          dma_16(p.b + (size_t)(kb * KBLK + kr) * p.N + min(n0 + 16 * c, p.N - 16), slot + DBM * KBLK + q * 1024);
+          dma_16_nt(p.b + (size_t)(kb * KBLK + kr) * p.N + min(n0 + 16 * c, p.N - 16), slot + DBM * KBLK + q * 1024);
         }
       } else if constexpr (B4) {
         // 16 rows of 64 bytes per instruction: lane l takes row 16q + l/4,
@@ -195,7 +197,7 @@ __device__ __forceinline__ void decode_item(const Params& p, uint8_t* smem, int 
         for (int q = 0; q < DBN / 16; ++q) {
           const int r = q * 16 + (lane >> 2);
           const int gn = min(n0 + r, p.N - 1);
-          dma_16(p.b + (size_t)gn * (p.K / 2) + (size_t)kb * BROW + (((lane & 3) ^ swz4(r)) << 4),
+          dma_16_nt(p.b + (size_t)gn * (p.K / 2) + (size_t)kb * BROW + (((lane & 3) ^ swz4(r)) << 4),
                  slot + DBM * KBLK + q * 1024);
         }
       } else {
@@ -203,7 +205,7 @@ __device__ __forceinline__ void decode_item(const Params& p, uint8_t* smem, int 
         for (int q = 0; q < DBN / 8; ++q) {
           const int r = q * 8 + lr;
           const int gn = min(n0 + r, p.N - 1);
-          dma_16(p.b + (size_t)gn * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4),
+          dma_16_nt(p.b + (size_t)gn * p.K + (size_t)kb * KBLK + (((lane & 7) ^ swz(r)) << 4),
                  slot + DBM * KBLK + q * 1024);
         }
       }

@@ -132,6 +132,12 @@ __device__ __forceinline__ void dma_16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
+// The same with the streaming (non-temporal) cache policy: for lines that one
+// load brings in once and nothing reads again.
+__device__ __forceinline__ void dma_16_nt(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
 __device__ __forceinline__ void dma_4(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(gptr), "s"(lds_addr) : "memory", "m0");
