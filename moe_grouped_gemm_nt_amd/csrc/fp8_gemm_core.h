@@ -391,6 +391,11 @@ __device__ __forceinline__ void dma_16s(const void* sbase, uint32_t voff, uint32
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
+// The same with the streaming (non-temporal) cache policy.
+__device__ __forceinline__ void dma_16s_nt(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // E8M0 = false: MFMA partials promoted by fp32 FMAs (any scales).
@@ -719,8 +724,15 @@ fp8_gemm_nt_kernel(PT p) {
         dma_16s(a_tile + i * a_kstep, a_off[k], smem_base + u * S::A_BYTES + (wave + S::NWAVES * k) * 1024);
       } else if (k < S::A_INSTR + S::B_INSTR) {
         const int j = k - S::A_INSTR;
-        dma_16s(b_tile + i * b_kstep, b_off[j],
-                smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
+        // a masked group's B columns go to one item per m-tile of the group
+        // (one for groups of up to BM rows): streaming policy; elsewhere the
+        // other row tiles read them again from the L2
+        if constexpr (MODE == kMasked)
+          dma_16s_nt(b_tile + i * b_kstep, b_off[j],
+                     smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
+        else
+          dma_16s(b_tile + i * b_kstep, b_off[j],
+                  smem_base + S::B_REGION + u * S::B_BYTES + (wave + S::NWAVES * j) * 1024);
       } else if (!S::SB_SEP || k == S::A_INSTR + S::B_INSTR) {
         // lanes past RS load the B scale (lane RS's copy is the one read)
         dma_4(s_src + (size_t)i * s_stride, smem_base + S::S_REGION + u * S::S_BYTES + wave * S::SA_PER_WAVE * 4);
